@@ -1,0 +1,232 @@
+"""CPU oracle for the TwoTower denoiser block step (fp64 numpy).
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call or link
+this module: only the test suite, the package smoke check and the benchmark's
+CPU-baseline leg use it. It shares no code, header, table or helper with the HIP
+path; the only thing both sides share is the seeded input module ``synth``.
+
+What it computes, each function citing the passage it follows. Page names:
+  [wiki]  "Nemotron-Labs-TwoTower" (aiwiki article summarising the paper and model card)
+  [mlx]   "Nemotron TwoTower · MLX" (README of the Apple-Silicon port)
+  [blog]  "Nemotron-TwoTower: Rethinking LLM Throughput via Decoupled Diffusion"
+
+Every function is the plain definition (or, for the commit rule, the algorithm's
+steps in the pages' order) in float64, with numpy's matmul/exp/max as the only
+library steps. No blocking, splitting or reordering beyond the definitions.
+
+Readings where the pages are silent (each also listed in the design notes):
+  * softmax scale is an explicit argument (1/sqrt(D) in every workload);
+  * grouped-query attention maps query head h to kv head floor(h / (Hq/Hkv));
+  * Q and K arrive already position-encoded, so the step itself is position-agnostic;
+  * confidence = the largest softmax probability at temperature 1, after the mask
+    token's logit is set to -inf (so the mask token is never emitted);
+  * the threshold test is ``conf >= gamma``;
+  * the completion floor commits the k = ceil(n_masked / (T - step)) most confident
+    masked positions when fewer than k clear gamma (ties: lower position first);
+  * argmax ties go to the lowest vocabulary id;
+  * the LM head is a bias-free product hidden . W^T with fp32 logits.
+
+Parity pins: every function here is pinned by the ``-m "not gpu"`` tests
+(brute force, closed forms, library special cases, invariants and a hand-worked
+commit trace); see tests/test_oracle_*.py.
+"""
+from __future__ import annotations
+
+import math
+from typing import Iterable, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+
+# ----------------------------------------------------------------------------- inputs
+
+def decode(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact float64 value of stored inputs: bf16 bit patterns (uint16) or float32."""
+    if dtype == "bf16":
+        u = np.asarray(x, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+        return u.view(np.float32).astype(np.float64)
+    if dtype == "f32":
+        return np.asarray(x, dtype=np.float32).astype(np.float64)
+    raise ValueError(dtype)
+
+
+# ----------------------------------------------------------------------------- attention
+
+def block_attention(inp: dict, dtype: str, rows: Optional[Iterable[Tuple[int, int, int]]] = None,
+                    return_probs: bool = False):
+    """Denoiser block attention ([wiki] "Architecture": the noisy block's queries attend over
+    the concatenation of the context tower's layer-i cache for the earlier blocks and the
+    denoiser's own layer-i keys/values for the current block; inside the block attention is
+    bidirectional, so no mask applies anywhere).
+
+    For sequence b, block position s, query head h, with kv head g = h // (Hq/Hkv):
+        K = [K_ctx[g, start_b : start_b + len_b] ; K_blk[b, :, g]]   (V likewise)
+        z = scale * K q_{b,s,h};  p = exp(z - max z) / sum exp(z - max z);  o = p^T V
+
+    inp: dict from synth.attn_inputs (q [B][S][Hq][D], k_blk/v_blk [B][S][Hkv][D],
+    k_ctx/v_ctx [Hkv][rows][D], ctx_start/ctx_len [B], scale).
+    rows: optional iterable of (b, s, h); then returns {(b, s, h): o} (and probs).
+    Otherwise returns o as float64 [B][S][Hq][D] (and probs per (b, g) if asked).
+    """
+    q = inp["q"]
+    B, S, Hq, D = q.shape
+    Hkv = inp["k_blk"].shape[2]
+    G = Hq // Hkv
+    scale = float(inp["scale"])
+    starts = np.asarray(inp["ctx_start"], dtype=np.int64)
+    lens = np.asarray(inp["ctx_len"], dtype=np.int64)
+
+    def keys_values(b: int, g: int):
+        a, n = int(starts[b]), int(lens[b])
+        K = np.concatenate([decode(inp["k_ctx"][g, a:a + n], dtype), decode(inp["k_blk"][b, :, g], dtype)], axis=0)
+        Vv = np.concatenate([decode(inp["v_ctx"][g, a:a + n], dtype), decode(inp["v_blk"][b, :, g], dtype)], axis=0)
+        return K, Vv
+
+    def attend(K, Vv, qvecs):
+        z = scale * (qvecs @ K.T)                    # [rows][keys]
+        z = z - z.max(axis=1, keepdims=True)
+        e = np.exp(z)
+        p = e / e.sum(axis=1, keepdims=True)
+        return p @ Vv, p
+
+    if rows is not None:
+        want = {}
+        for (b, s, h) in rows:
+            want.setdefault((int(b), int(h) // G), []).append((int(b), int(s), int(h)))
+        out, probs = {}, {}
+        for (b, g), lst in want.items():
+            K, Vv = keys_values(b, g)
+            qv = np.stack([decode(q[bb, s, h], dtype) for (bb, s, h) in lst])
+            o, p = attend(K, Vv, qv)
+            for i, key in enumerate(lst):
+                out[key] = o[i]
+                probs[key] = p[i]
+        return (out, probs) if return_probs else out
+
+    out = np.zeros((B, S, Hq, D), dtype=np.float64)
+    probs = {}
+    for b in range(B):
+        for g in range(Hkv):
+            K, Vv = keys_values(b, g)
+            qg = decode(q[b, :, g * G:(g + 1) * G, :], dtype).reshape(S * G, D)
+            o, p = attend(K, Vv, qg)
+            out[b, :, g * G:(g + 1) * G, :] = o.reshape(S, G, D)
+            probs[(b, g)] = p.reshape(S, G, -1)
+    return (out, probs) if return_probs else out
+
+
+# ----------------------------------------------------------------------------- LM head
+
+def lmhead_logits(hidden: np.ndarray, w: np.ndarray, dtype: str) -> np.ndarray:
+    """Vocabulary logits of every block position ([wiki] "Block-wise generation": each
+    denoising step predicts all currently masked positions). logits = hidden . W^T, float64,
+    with hidden [M][H] and W [V][H]; no bias, no norm (the pages name none)."""
+    return decode(hidden, dtype) @ decode(w, dtype).T
+
+
+def lmhead_entries(hidden: np.ndarray, w: np.ndarray, dtype: str,
+                   pairs: Sequence[Tuple[int, int]]) -> np.ndarray:
+    """Selected logits (m, v) of the same product, one dot product each."""
+    return np.array([float(decode(hidden[m], dtype) @ decode(w[v], dtype)) for (m, v) in pairs])
+
+
+# ----------------------------------------------------------------------------- confidence
+
+def masked_softmax(row: np.ndarray, mask_id: int) -> np.ndarray:
+    """Softmax of one logits row with the mask token excluded ([wiki] "Block-wise
+    generation": predictions are constrained so the mask token itself is never emitted);
+    the mask entry's logit becomes -inf, so its probability is 0."""
+    l = np.array(row, dtype=np.float64)
+    l[mask_id] = -np.inf
+    m = l.max()
+    e = np.exp(l - m)
+    return e / e.sum()
+
+
+def reduce_row(row: np.ndarray, mask_id: int) -> Tuple[float, int]:
+    """(confidence, prediction) of one position: the largest probability of the masked
+    softmax and the lowest vocabulary id that attains it ([wiki] "Block-wise generation";
+    [blog] "Adaptive Step-wise Generation")."""
+    l = np.array(row, dtype=np.float64)
+    l[mask_id] = -np.inf
+    m = l.max()
+    a = int(np.flatnonzero(l == m)[0])
+    s = float(np.exp(l - m).sum())
+    return 1.0 / s, a
+
+
+# ----------------------------------------------------------------------------- commit
+
+def commit_block(conf: Sequence[float], pred: Sequence[int], tokens: np.ndarray, mask_bits: int,
+                 S: int, step: int, T: int, gamma: float) -> Tuple[np.ndarray, int, int, List[int]]:
+    """One step of confidence unmasking for one block ([wiki] "Block-wise generation":
+    every masked position is predicted in parallel; predictions whose confidence clears
+    gamma are committed, the rest stay masked; a floor makes the block finish within T
+    steps; decoded positions stay fixed).
+
+    Steps, in order:
+      masked set Mk = positions whose bit is set (empty: nothing changes, n_masked = 0)
+      C = {i in Mk : conf_i >= gamma}
+      k = ceil(|Mk| / (T - step))                      (the floor)
+      if |C| < k: C = the k positions of Mk with the largest confidence (ties: lower i)
+      for i in C: token_i = pred_i, clear bit i
+      n_masked = |Mk| - |C|   (next step's timestep is n_masked / S)
+    Returns (tokens, mask_bits, n_masked, committed positions)."""
+    tokens = np.array(tokens, dtype=np.int32, copy=True)
+    Mk = [i for i in range(S) if (mask_bits >> i) & 1]
+    if not Mk:
+        return tokens, mask_bits, 0, []
+    C = [i for i in Mk if conf[i] >= gamma]
+    k = -(-len(Mk) // (T - step))
+    if len(C) < k:
+        C = sorted(Mk, key=lambda i: (-conf[i], i))[:k]
+    for i in sorted(C):
+        tokens[i] = pred[i]
+        mask_bits &= ~(1 << i)
+    return tokens, mask_bits, len(Mk) - len(C), sorted(C)
+
+
+def confidence_unmask(logits: np.ndarray, tokens: np.ndarray, mask_bits: np.ndarray, S: int,
+                      step: int, T: int, gamma: float, mask_id: int):
+    """The whole unmask call over B blocks: logits [B*S][V] (any float dtype, read as float64),
+    tokens int32 [B][S], mask_bits uint64 [B]. Rows of positions that are not masked at the
+    start of the step are not read and keep their tokens.
+
+    Returns dict(tokens, mask_bits, n_masked, conf, pred, committed) where conf/pred are
+    (-1.0, -1) for positions not masked at step start."""
+    B = tokens.shape[0]
+    tok_out = np.array(tokens, dtype=np.int32, copy=True)
+    bits_out = np.array(mask_bits, dtype=np.uint64, copy=True)
+    n_masked = np.zeros(B, dtype=np.int32)
+    conf = np.full((B, S), -1.0)
+    pred = np.full((B, S), -1, dtype=np.int64)
+    committed = []
+    for b in range(B):
+        bits = int(mask_bits[b])
+        for i in range(S):
+            if (bits >> i) & 1:
+                c, a = reduce_row(logits[b * S + i], mask_id)
+                conf[b, i], pred[b, i] = c, a
+        t, nb, nm, C = commit_block(conf[b], pred[b], tokens[b], bits, S, step, T, gamma)
+        tok_out[b], bits_out[b], n_masked[b] = t, np.uint64(nb), nm
+        committed.append(C)
+    return dict(tokens=tok_out, mask_bits=bits_out, n_masked=n_masked, conf=conf, pred=pred,
+                committed=committed)
+
+
+# ----------------------------------------------------------------------------- one step
+
+def denoise_step(attn_layers: Sequence[dict], hidden: np.ndarray, w: np.ndarray, dtype: str,
+                 spike_tok: np.ndarray, spike_val: np.ndarray, tokens: np.ndarray,
+                 mask_bits: np.ndarray, S: int, step: int, T: int, gamma: float, mask_id: int):
+    """One denoiser block step as the benchmark runs it: block attention for every layer
+    (outputs are returned; the synthetic workloads have no projections to chain them), the
+    LM head, the synthetic logit spikes (an input-construction step, not part of the method),
+    then confidence unmasking."""
+    outs = [block_attention(inp, dtype) for inp in attn_layers]
+    logits = lmhead_logits(hidden, w, dtype)
+    logits[np.arange(logits.shape[0]), spike_tok] += spike_val.astype(np.float64)
+    res = confidence_unmask(logits, tokens, mask_bits, S, step, T, gamma, mask_id)
+    res["attn"] = outs
+    res["logits"] = logits
+    return res
