@@ -1,0 +1,45 @@
+// Shared types and helpers of the gfx950 kernels behind tt.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "tt.h"
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+#define TT_WAVE 64
+
+static inline size_t tt_align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Map the outcome of a kernel launch to a status code.
+static inline int tt_launch_status() {
+  return hipGetLastError() == hipSuccess ? TT_OK : TT_ERR_HIP;
+}
+
+// Workspace protocol shared by the calls that take one (see tt.h).
+//   returns 1 when the caller only asked for the size (nothing to launch), 0 to proceed,
+//   or a negative status.
+static inline int tt_workspace_check(void* ws, size_t* ws_bytes, size_t need) {
+  if (ws_bytes == nullptr) return TT_ERR_ARG;
+  if (ws == nullptr) {
+    *ws_bytes = need;
+    return 1;
+  }
+  if (*ws_bytes < need) return TT_ERR_WORKSPACE;
+  return 0;
+}
+
+// Cross-lane helpers (wave64).
+__device__ __forceinline__ float tt_shfl_xor(float v, int mask) { return __shfl_xor(v, mask, TT_WAVE); }
+__device__ __forceinline__ int tt_shfl_xor(int v, int mask) { return __shfl_xor(v, mask, TT_WAVE); }
+
+// exp2 on the hardware transcendental unit (v_exp_f32): exact at 0, returns 0 for -inf.
+__device__ __forceinline__ float tt_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

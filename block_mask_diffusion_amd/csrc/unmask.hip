@@ -1,0 +1,213 @@
+// Confidence unmasking ("Nemotron-Labs-TwoTower" wiki page, section "Block-wise generation").
+//
+// Two kernels on the caller's stream:
+//   unmask_partial  one workgroup per (still-masked row, 4096-entry vocabulary chunk): streams the
+//                   chunk once with coalesced 16-byte loads and reduces it to (max, lowest argmax,
+//                   sum of exp(l - max)), the mask id's logit counting as -inf. HBM-bound: each
+//                   logit of a masked row is read exactly once; rows already committed are skipped
+//                   without reading anything but their mask word.
+//   unmask_commit   one wave per block: lane i merges row i's chunk partials in a fixed order
+//                   (deterministic), gets conf = 1 / sum and the prediction, then applies the
+//                   threshold, the completion floor and the in-place token / bitmap update.
+#include "common.h"
+
+namespace {
+
+constexpr int UM_THREADS = 256;
+constexpr int UM_PER_THREAD = 16;
+constexpr int UM_CHUNK = UM_THREADS * UM_PER_THREAD;  // vocabulary entries per workgroup
+constexpr float LOG2E = 1.4426950408889634f;
+
+struct alignas(16) Partial {
+  float m;  // chunk max (-inf when the chunk holds no eligible entry)
+  float s;  // sum of exp(l - m) over the chunk
+  int a;    // lowest index attaining m (INT32_MAX when none)
+  int pad;
+};
+
+// Merge two (max, argmax, sum) triples; `a` ties resolve to the lower index.
+__device__ __forceinline__ void merge(float& m, int& a, float& s, float m2, int a2, float s2) {
+  float M = fmaxf(m, m2);
+  if (M == -INFINITY) return;  // both empty
+  float t1 = (m == -INFINITY) ? 0.f : s * tt_exp2((m - M) * LOG2E);
+  float t2 = (m2 == -INFINITY) ? 0.f : s2 * tt_exp2((m2 - M) * LOG2E);
+  int an = (m2 > m) ? a2 : ((m > m2) ? a : min(a, a2));
+  m = M;
+  a = an;
+  s = t1 + t2;
+}
+
+template <bool VEC4>
+__global__ __launch_bounds__(UM_THREADS) void unmask_partial(const float* __restrict__ logits,
+                                                             const uint64_t* __restrict__ mask_bits,
+                                                             Partial* __restrict__ ws, int S, int V,
+                                                             int nchunk, int mask_id) {
+  const int r = blockIdx.x / nchunk;
+  const int c = blockIdx.x - r * nchunk;
+  const int b = r / S, i = r - b * S;
+  if (!((mask_bits[b] >> i) & 1ull)) return;  // committed rows are never read
+  const float* row = logits + (size_t)r * V;
+  const int t = threadIdx.x;
+  const int v0 = c * UM_CHUNK;
+
+  float x[UM_PER_THREAD];
+  int idx[UM_PER_THREAD];
+  if (VEC4) {
+    // slot k: index v0 + (k/4)*1024 + 4t + k%4 -> each load instruction covers 4 KiB contiguous
+#pragma unroll
+    for (int q = 0; q < UM_PER_THREAD / 4; ++q) {
+      int base = v0 + q * (UM_THREADS * 4) + 4 * t;
+      f32x4 val;
+      if (base + 3 < V) {
+        val = *reinterpret_cast<const f32x4*>(row + base);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) val[e] = (base + e < V) ? row[base + e] : -INFINITY;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[4 * q + e] = val[e];
+        idx[4 * q + e] = base + e;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < UM_PER_THREAD; ++k) {
+      int v = v0 + k * UM_THREADS + t;
+      x[k] = (v < V) ? row[v] : -INFINITY;
+      idx[k] = v;
+    }
+  }
+  // the mask token never competes; indices grow with k, so a strict '>' keeps the lowest index
+  float m = -INFINITY;
+  int a = INT32_MAX;
+#pragma unroll
+  for (int k = 0; k < UM_PER_THREAD; ++k) {
+    if (idx[k] == mask_id) x[k] = -INFINITY;
+    if (x[k] > m) {
+      m = x[k];
+      a = idx[k];
+    }
+  }
+  float s = 0.f;
+  if (m != -INFINITY) {
+    const float mb = m * LOG2E;
+#pragma unroll
+    for (int k = 0; k < UM_PER_THREAD; ++k) s += tt_exp2(fmaf(x[k], LOG2E, -mb));
+  }
+  // wave reduction (fixed butterfly order)
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    float m2 = tt_shfl_xor(m, off);
+    int a2 = tt_shfl_xor(a, off);
+    float s2 = tt_shfl_xor(s, off);
+    merge(m, a, s, m2, a2, s2);
+  }
+  __shared__ float sm[UM_THREADS / TT_WAVE], ss[UM_THREADS / TT_WAVE];
+  __shared__ int sa[UM_THREADS / TT_WAVE];
+  const int w = t / TT_WAVE;
+  if ((t & (TT_WAVE - 1)) == 0) {
+    sm[w] = m;
+    ss[w] = s;
+    sa[w] = a;
+  }
+  __syncthreads();
+  if (t == 0) {
+    for (int k = 1; k < UM_THREADS / TT_WAVE; ++k) merge(m, a, s, sm[k], sa[k], ss[k]);
+    Partial p;
+    p.m = m;
+    p.s = s;
+    p.a = a;
+    p.pad = 0;
+    ws[(size_t)r * nchunk + c] = p;
+  }
+}
+
+__global__ __launch_bounds__(TT_WAVE) void unmask_commit(const Partial* __restrict__ ws,
+                                                         int32_t* __restrict__ tokens,
+                                                         uint64_t* __restrict__ mask_bits,
+                                                         int32_t* __restrict__ n_masked,
+                                                         float* __restrict__ conf_out,
+                                                         int32_t* __restrict__ pred_out, int S,
+                                                         int nchunk, int step, int num_steps,
+                                                         float gamma) {
+  const int b = blockIdx.x;
+  const int i = threadIdx.x;
+  const uint64_t bits = mask_bits[b];
+  const bool masked = (i < S) && ((bits >> i) & 1ull);
+  float conf = -1.f;
+  int pred = -1;
+  if (masked) {
+    const Partial* p = ws + (size_t)(b * S + i) * nchunk;
+    float m = -INFINITY, s = 0.f;
+    int a = INT32_MAX;
+    for (int c = 0; c < nchunk; ++c) {  // fixed order: bitwise reproducible
+      Partial q = p[c];
+      merge(m, a, s, q.m, q.a, q.s);
+    }
+    conf = 1.f / s;
+    pred = a;
+  }
+  const uint64_t mk = __ballot(masked);
+  const int nM = __popcll(mk);
+  uint64_t sel = 0;
+  if (nM > 0) {
+    sel = __ballot(masked && conf >= gamma);
+    const int left = num_steps - step;
+    const int k = (nM + left - 1) / left;  // completion floor
+    if (__popcll(sel) < k) {
+      int rank = 0;  // place among the masked positions: higher conf first, then lower position
+      for (int j = 0; j < S; ++j) {
+        float cj = __shfl(conf, j, TT_WAVE);
+        bool mj = (mk >> j) & 1ull;
+        rank += (mj && (cj > conf || (cj == conf && j < i))) ? 1 : 0;
+      }
+      sel = __ballot(masked && rank < k);
+    }
+  }
+  if ((sel >> i) & 1ull) tokens[(size_t)b * S + i] = pred;
+  if (i < S) {
+    if (conf_out) conf_out[(size_t)b * S + i] = conf;
+    if (pred_out) pred_out[(size_t)b * S + i] = pred;
+  }
+  if (i == 0) {
+    mask_bits[b] = bits & ~sel;
+    n_masked[b] = nM - __popcll(sel);
+  }
+}
+
+}  // namespace
+
+extern "C" int tt_confidence_unmask(const float* logits, int32_t* tokens, uint64_t* mask_bits,
+                                    int32_t* n_masked, float* conf_out, int32_t* pred_out, int B,
+                                    int S, int V, int step, int num_steps, float gamma,
+                                    int mask_id, void* workspace, size_t* workspace_bytes,
+                                    void* stream) {
+  if (!logits || !tokens || !mask_bits || !n_masked || !workspace_bytes) return TT_ERR_ARG;
+  if (B <= 0 || S <= 0 || V < 2) return TT_ERR_ARG;
+  if (mask_id < 0 || mask_id >= V) return TT_ERR_ARG;
+  if (num_steps <= 0 || step < 0 || step >= num_steps) return TT_ERR_ARG;
+  if (gamma != gamma) return TT_ERR_ARG;
+  if (S > 64) return TT_ERR_UNSUPPORTED;
+  const size_t rows = (size_t)B * S;
+  const int nchunk = (V + UM_CHUNK - 1) / UM_CHUNK;
+  if (rows * (size_t)nchunk > (size_t)INT32_MAX) return TT_ERR_UNSUPPORTED;
+  const size_t need = rows * nchunk * sizeof(Partial);
+  int st = tt_workspace_check(workspace, workspace_bytes, need);
+  if (st != 0) return st < 0 ? st : TT_OK;
+  if ((uintptr_t)workspace % alignof(Partial)) return TT_ERR_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  Partial* ws = (Partial*)workspace;
+  const bool vec4 = (V % 4 == 0) && ((uintptr_t)logits % 16 == 0);
+  dim3 grid((unsigned)(rows * nchunk));
+  if (vec4)
+    hipLaunchKernelGGL(unmask_partial<true>, grid, dim3(UM_THREADS), 0, s, logits, mask_bits, ws,
+                       S, V, nchunk, mask_id);
+  else
+    hipLaunchKernelGGL(unmask_partial<false>, grid, dim3(UM_THREADS), 0, s, logits, mask_bits, ws,
+                       S, V, nchunk, mask_id);
+  if (tt_launch_status() != TT_OK) return TT_ERR_HIP;
+  hipLaunchKernelGGL(unmask_commit, dim3(B), dim3(TT_WAVE), 0, s, ws, tokens, mask_bits, n_masked,
+                     conf_out, pred_out, S, nchunk, step, num_steps, gamma);
+  return tt_launch_status();
+}

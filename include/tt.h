@@ -1,0 +1,132 @@
+/*
+ * tt.h — C ABI of the TwoTower denoiser block step on AMD CDNA4 (gfx950).
+ *
+ * One denoising step of a masked block ("Nemotron-Labs-TwoTower" wiki page, sections
+ * "Architecture" and "Block-wise generation"): the block's queries attend, with grouped-query
+ * heads, over [context-tower cache ; the block's own keys/values] with no mask (bidirectional
+ * inside the block); an LM-head product turns the block's hidden states into vocabulary logits;
+ * confidence unmasking commits every still-masked position whose top probability reaches gamma
+ * and keeps the rest masked, with a floor that finishes the block within the step budget.
+ *
+ * Conventions shared by every call:
+ *   - Every pointer argument is a DEVICE pointer to memory the caller owns, except
+ *     `workspace_bytes`, which is a host pointer. The library keeps no pointer after it returns
+ *     and has no mutable global state; calls on different streams do not interact, except that
+ *     they must not share a workspace or an in/out buffer while both are in flight.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Calls only enqueue work: TT_OK
+ *     means "launched"; a device fault surfaces at the caller's next synchronisation.
+ *   - Arguments are validated on the host before anything is launched. Any error return means
+ *     nothing was launched and nothing was written.
+ *   - `dtype` is TT_F32 (IEEE fp32 storage) or TT_BF16 (bfloat16 storage). Arithmetic is fp32
+ *     (MFMA fp32 accumulation) in both cases; bf16 outputs are rounded to nearest-even.
+ *   - Workspace protocol (calls that take one): with workspace == NULL the call stores the
+ *     required byte count in *workspace_bytes, returns TT_OK and launches nothing. Otherwise
+ *     *workspace_bytes must hold the size of `workspace` (>= the required size, else
+ *     TT_ERR_WORKSPACE); the workspace needs no initialisation and is scratch afterwards.
+ */
+#ifndef TT_H
+#define TT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum tt_dtype { TT_F32 = 0, TT_BF16 = 1 };
+
+enum tt_status {
+  TT_OK = 0,
+  TT_ERR_ARG = -1,          /* invalid argument (null pointer, bad size, NaN parameter, ...) */
+  TT_ERR_UNSUPPORTED = -2,  /* valid but outside what the kernels implement (head_dim, S, dtype) */
+  TT_ERR_WORKSPACE = -3,    /* workspace smaller than required */
+  TT_ERR_HIP = -4           /* the HIP runtime reported an error at launch */
+};
+
+/*
+ * tt_block_attn — denoiser block attention for one layer ("Nemotron-Labs-TwoTower" wiki page,
+ * section "Architecture": the noisy block's queries attend over the context tower's layer-i
+ * cache for the earlier blocks concatenated with the denoiser's own layer-i keys and values
+ * for the current block; bidirectional inside the block, so no mask applies).
+ *
+ * For every sequence b, block position s and query head h (kv head g = h / (Hq/Hkv)):
+ *   keys   = [ k_ctx[g][ctx_start[b] .. ctx_start[b]+ctx_len[b]) ; k_blk[b][0..S)[g] ]
+ *   values = the same rows of v_ctx / v_blk
+ *   out[b][s][h] = softmax(softmax_scale * keys . q[b][s][h]) . values
+ *
+ * Layouts (row-major, element = dtype):
+ *   q, out       [B][S][Hq][D]
+ *   k_blk, v_blk [B][S][Hkv][D]
+ *   k_ctx, v_ctx [Hkv][ctx_rows][D]   (sequences packed along ctx_rows)
+ *   ctx_start, ctx_len  int32 [B] on the device; ctx_len[b] may be 0.
+ * Caller's contract (not checked): 0 <= ctx_len[b] <= max_prefix and
+ *   ctx_start[b] + ctx_len[b] <= ctx_rows. max_prefix sizes the launch.
+ * Supported: D in {64, 128}; S*(Hq/Hkv) <= 256; dtype TT_F32 or TT_BF16.
+ * Errors: TT_ERR_ARG for null pointers, B/S/Hq/Hkv <= 0, Hq % Hkv != 0, ctx_rows < 0,
+ *   max_prefix < 0, max_prefix > 0 with null k_ctx/v_ctx, non-finite or non-positive scale;
+ *   TT_ERR_UNSUPPORTED for D or S*G outside the supported set; TT_ERR_WORKSPACE; TT_ERR_HIP.
+ * Workspace: split-K partial results (fp32), sized from B, Hkv, S*G, D and max_prefix.
+ */
+int tt_block_attn(const void* q, const void* k_blk, const void* v_blk,
+                  const void* k_ctx, const void* v_ctx,
+                  const int32_t* ctx_start, const int32_t* ctx_len,
+                  void* out,
+                  int B, int S, int Hq, int Hkv, int D, int64_t ctx_rows, int max_prefix,
+                  float softmax_scale, int dtype,
+                  void* workspace, size_t* workspace_bytes, void* stream);
+
+/*
+ * tt_lmhead_logits — vocabulary logits of every block position ("Nemotron-Labs-TwoTower" wiki
+ * page, section "Block-wise generation": each step predicts all masked positions in parallel).
+ *
+ *   logits[m][v] = sum_k hidden[m][k] * w[v][k]        (no bias, no normalisation)
+ *
+ * Layouts: hidden [M][H] (dtype), w [V][H] (dtype), logits [M][V] fp32 (always fp32, so the
+ * confidence test that follows sees full-precision logits).
+ * Supported: H % 32 == 0; dtype TT_F32 or TT_BF16.
+ * Errors: TT_ERR_ARG for null pointers or M, H, V <= 0; TT_ERR_UNSUPPORTED for H % 32 != 0 or
+ *   an unknown dtype; TT_ERR_HIP.
+ */
+int tt_lmhead_logits(const void* hidden, const void* w, float* logits,
+                     int M, int H, int V, int dtype, void* stream);
+
+/*
+ * tt_confidence_unmask — one confidence-unmasking step over B blocks ("Nemotron-Labs-TwoTower"
+ * wiki page, section "Block-wise generation"; the operating point gamma = 0.8, S = 16, 16 steps
+ * per block is given there; mask id 3 comes from the MLX port's configuration table).
+ *
+ * For each block b, with Mk = the positions whose bit is set in mask_bits[b] at entry:
+ *   conf_i, pred_i = max and lowest argmax of softmax(logits row) with the mask id's logit
+ *                    treated as -inf (so the mask token is never predicted), i in Mk;
+ *   C = { i in Mk : conf_i >= gamma };   k = ceil(|Mk| / (num_steps - step));
+ *   if |C| < k, C = the k most confident positions of Mk (ties: lower position first);
+ *   tokens[b][i] = pred_i and bit i cleared for i in C; n_masked[b] = |Mk| - |C|.
+ * Positions outside Mk are never read (their logits rows may hold anything) nor written.
+ * Layouts: logits fp32 [B*S][V] (row b*S+i is position i of block b); tokens int32 [B][S]
+ *   (in/out); mask_bits uint64 [B] (in/out; bit i = position i still masked); n_masked int32 [B]
+ *   (out). conf_out fp32 [B*S] and pred_out int32 [B*S] are optional (NULL = not written); when
+ *   given they receive (conf_i, pred_i) for positions in Mk and (-1.0f, -1) for the others.
+ * Supported: 1 <= S <= 64.
+ * Errors: TT_ERR_ARG for null required pointers, B <= 0, S <= 0, V < 2, mask_id outside
+ *   [0, V), num_steps <= 0, step outside [0, num_steps), NaN gamma; TT_ERR_UNSUPPORTED for
+ *   S > 64; TT_ERR_WORKSPACE; TT_ERR_HIP. Any finite or infinite gamma is legal (gamma > 1
+ *   commits exactly the floor's k per step; gamma <= 0 commits every masked position).
+ * Workspace: per-row, per-vocabulary-chunk partial reductions, sized from B*S and V.
+ */
+int tt_confidence_unmask(const float* logits, int32_t* tokens, uint64_t* mask_bits,
+                         int32_t* n_masked, float* conf_out, int32_t* pred_out,
+                         int B, int S, int V, int step, int num_steps, float gamma, int mask_id,
+                         void* workspace, size_t* workspace_bytes, void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* tt_status_string(int status);
+
+/* Library ABI version: (major << 16) | minor. */
+int tt_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TT_H */

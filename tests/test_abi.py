@@ -1,0 +1,125 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol include/tt.h declares, and its
+host-side validation and workspace queries behave as documented. Nothing here launches a
+kernel: every call below returns before any HIP work (an error, or a size query)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_mask_diffusion_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+P = ctypes.c_void_p(4096)  # non-null placeholder: never dereferenced by the paths tested here
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "tt.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(tt_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    names = _declared()
+    assert set(names) == set(_lib.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.tt_abi_version() >> 16 == 1
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4):
+        assert _lib.status_string(code).startswith("TT_")
+    assert _lib.status_string(7) == "unknown status"
+
+
+def _attn(**kw):
+    a = dict(q=P, kb=P, vb=P, kc=P, vc=P, cs=P, cl=P, out=P, B=1, S=16, Hq=32, Hkv=2, D=128,
+             ctx_rows=2048, max_prefix=2048, scale=0.088, dtype=_lib.TT_BF16)
+    a.update(kw)
+    n = ctypes.c_size_t(0)
+    st = _lib.load().tt_block_attn(a["q"], a["kb"], a["vb"], a["kc"], a["vc"], a["cs"], a["cl"], a["out"],
+                                   a["B"], a["S"], a["Hq"], a["Hkv"], a["D"], a["ctx_rows"],
+                                   a["max_prefix"], a["scale"], a["dtype"], None, ctypes.byref(n), None)
+    return st, n.value
+
+
+def test_attn_workspace_query_and_size():
+    st, n = _attn()
+    assert st == 0
+    # 2 units, 4128 keys -> ceil(4128/128) = 33 workgroups; slots = 33 + 2, R = 256 rows, D = 128
+    slots, R, D = 35, 256, 128
+    expect = -(-(slots * R * D * 4) // 256) * 256 + -(-(slots * R * 8) // 256) * 256
+    assert n == expect
+    st, n4 = _attn(B=4, max_prefix=131072, ctx_rows=4 * 131072)
+    assert st == 0 and n4 == -(-((256 + 8) * R * D * 4) // 256) * 256 + -(-((256 + 8) * R * 8) // 256) * 256
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(out=None), -1), (dict(cs=None), -1), (dict(kc=None), -1),
+    (dict(B=0), -1), (dict(S=0), -1), (dict(Hq=33), -1), (dict(Hkv=0), -1), (dict(max_prefix=-1), -1),
+    (dict(scale=float("nan")), -1), (dict(scale=0.0), -1), (dict(scale=float("inf")), -1),
+    (dict(ctx_rows=-1), -1),
+    (dict(D=96), -2), (dict(D=256), -2), (dict(dtype=5), -2), (dict(S=17), -2), (dict(B=1025), -2),
+])
+def test_attn_argument_errors(kw, code):
+    assert _attn(**kw)[0] == code
+
+
+def test_attn_null_context_allowed_without_prefix():
+    assert _attn(kc=None, vc=None, max_prefix=0, ctx_rows=0)[0] == 0
+
+
+def test_attn_workspace_too_small():
+    n = ctypes.c_size_t(100)
+    st = _lib.load().tt_block_attn(P, P, P, P, P, P, P, P, 1, 16, 32, 2, 128, 2048, 2048, 0.088,
+                                   _lib.TT_BF16, P, ctypes.byref(n), None)
+    assert st == _lib.TT_ERR_WORKSPACE
+
+
+def _lm(**kw):
+    a = dict(h=P, w=P, out=P, M=16, H=2688, V=131072, dtype=_lib.TT_BF16)
+    a.update(kw)
+    return _lib.load().tt_lmhead_logits(a["h"], a["w"], a["out"], a["M"], a["H"], a["V"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(h=None), -1), (dict(w=None), -1), (dict(out=None), -1), (dict(M=0), -1), (dict(H=-32), -1),
+    (dict(V=0), -1), (dict(H=2680), -2), (dict(dtype=3), -2), (dict(h=ctypes.c_void_p(4098)), -1),
+])
+def test_lmhead_argument_errors(kw, code):
+    assert _lm(**kw) == code
+
+
+def _um(ws=None, nbytes=0, **kw):
+    a = dict(lg=P, tok=P, bits=P, nm=P, B=1, S=16, V=131072, step=0, T=16, gamma=0.8, mask_id=3)
+    a.update(kw)
+    n = ctypes.c_size_t(nbytes)
+    st = _lib.load().tt_confidence_unmask(a["lg"], a["tok"], a["bits"], a["nm"], None, None, a["B"], a["S"],
+                                          a["V"], a["step"], a["T"], a["gamma"], a["mask_id"], ws,
+                                          ctypes.byref(n), None)
+    return st, n.value
+
+
+def test_unmask_workspace_query():
+    st, n = _um()
+    assert st == 0 and n == 16 * 32 * 16        # rows x 4096-entry chunks x 16 bytes
+    st, n = _um(B=32, V=1000)
+    assert st == 0 and n == 512 * 1 * 16
+    assert _um(ws=P, nbytes=10)[0] == _lib.TT_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(lg=None), -1), (dict(tok=None), -1), (dict(bits=None), -1), (dict(nm=None), -1),
+    (dict(B=0), -1), (dict(S=0), -1), (dict(V=1), -1), (dict(mask_id=-1), -1), (dict(mask_id=131072), -1),
+    (dict(T=0), -1), (dict(step=16), -1), (dict(step=-1), -1), (dict(gamma=float("nan")), -1),
+    (dict(S=65), -2),
+])
+def test_unmask_argument_errors(kw, code):
+    assert _um(**kw)[0] == code
+
+
+def test_unmask_any_gamma_is_legal():
+    for g in (float("inf"), float("-inf"), 2.0, 0.0, -1.0):
+        assert _um(gamma=g)[0] == 0

@@ -1,0 +1,109 @@
+"""GPU parity of tt_block_attn against the oracle on the same seeded inputs."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import ATOL_BF16, ATOL_F32, attn_dev
+
+pytestmark = pytest.mark.gpu
+
+bmd = pytest.importorskip("block_mask_diffusion_amd")
+
+
+def _run(inp_np, wl):
+    d = attn_dev(inp_np)
+    out = bmd.tt_block_attn(d["q"], d["k_blk"], d["v_blk"], d["k_ctx"], d["v_ctx"], d["ctx_start"],
+                            d["ctx_len"], max_prefix=wl.max_prefix, softmax_scale=d["scale"])
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64)
+
+
+def _wl(wid=1, **kw):
+    wl = synth.workload(wid, **kw)
+    return wl
+
+
+def _full_check(wl, layer=0):
+    inp = synth.attn_inputs(wl, layer)
+    got = _run(inp, wl)
+    ref = oracle.block_attention(inp, wl.dtype)
+    err = float(np.max(np.abs(got - ref)))
+    tol = ATOL_BF16 if wl.dtype == "bf16" else ATOL_F32
+    assert err <= tol, err
+    return got, ref
+
+
+def test_tiny_fp32_workload():
+    _full_check(synth.workload(0))
+
+
+@pytest.mark.parametrize("prefixes", [[0], [1], [63], [64], [65], [0, 100, 1000], [777, 5, 130]])
+def test_bf16_several_tiles_and_ragged_tails(prefixes):
+    wl = _wl(1, B=len(prefixes), prefixes=prefixes)
+    wl.wid = 400 + sum(prefixes) % 101
+    _full_check(wl)
+
+
+@pytest.mark.parametrize("S,Hq,Hkv,D,dtype", [(16, 32, 2, 64, "bf16"), (8, 8, 2, 128, "bf16"),
+                                              (1, 4, 4, 128, "bf16"), (16, 16, 1, 128, "bf16"),
+                                              (5, 12, 3, 64, "bf16"), (16, 4, 1, 64, "f32"),
+                                              (16, 8, 2, 128, "f32"), (3, 2, 1, 64, "f32")])
+def test_head_layouts(S, Hq, Hkv, D, dtype):
+    wl = _wl(1, B=2, S=S, Hq=Hq, Hkv=Hkv, D=D, dtype=dtype, prefixes=[300, 47])
+    wl.wid = 500 + S * Hq + D
+    _full_check(wl)
+
+
+def test_workload_1_full():
+    _full_check(synth.workload(1))
+
+
+def test_workload_2_full():
+    _full_check(synth.workload(2))
+
+
+def _sampled_check(wl, layer=0, n=48, seed=0):
+    inp = synth.attn_inputs(wl, layer)
+    got = _run(inp, wl)
+    g = np.random.default_rng(seed)
+    rows = [(int(g.integers(wl.B)), int(g.integers(wl.S)), int(g.integers(wl.Hq))) for _ in range(n)]
+    rows += [(0, 0, 0), (wl.B - 1, wl.S - 1, wl.Hq - 1)]
+    ref = oracle.block_attention(inp, wl.dtype, rows=rows)
+    err = max(float(np.max(np.abs(got[r] - ref[r]))) for r in rows)
+    assert err <= ATOL_BF16, err
+    # every output is a convex combination of value rows: bounded by their extremes
+    assert np.all(np.isfinite(got))
+    vmax = max(float(np.abs(oracle.decode(inp["v_ctx"][:, :4096], "bf16")).max()), 6.0)
+    assert float(np.abs(got).max()) <= vmax
+
+
+def test_workload_3_ragged_sampled():
+    _sampled_check(synth.workload(3))
+
+
+def test_workload_4_one_layer_sampled():
+    _sampled_check(synth.workload(4), layer=5)
+
+
+def test_block_key_permutation_invariance():
+    wl = _wl(1, B=2, prefixes=[200, 1500])
+    wl.wid = 601
+    inp = synth.attn_inputs(wl)
+    base = _run(inp, wl)
+    perm = np.random.default_rng(1).permutation(wl.S)
+    inp2 = dict(inp, k_blk=inp["k_blk"][:, perm].copy(), v_blk=inp["v_blk"][:, perm].copy())
+    assert float(np.max(np.abs(_run(inp2, wl) - base))) <= 2e-3
+    inp3 = dict(inp, q=inp["q"][:, perm].copy())
+    assert float(np.max(np.abs(_run(inp3, wl) - base[:, perm]))) <= 2e-3
+
+
+def test_deterministic():
+    wl = synth.workload(3)
+    inp = synth.attn_inputs(wl)
+    d = attn_dev(inp)
+    outs = [bmd.tt_block_attn(d["q"], d["k_blk"], d["v_blk"], d["k_ctx"], d["v_ctx"], d["ctx_start"],
+                              d["ctx_len"], max_prefix=wl.max_prefix) for _ in range(2)]
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))

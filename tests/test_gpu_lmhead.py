@@ -1,0 +1,83 @@
+"""GPU parity of tt_lmhead_logits against the oracle on the same seeded inputs."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import ATOL_BF16, ATOL_F32, dev
+
+pytestmark = pytest.mark.gpu
+
+bmd = pytest.importorskip("block_mask_diffusion_amd")
+
+
+def _run(inp):
+    out = bmd.tt_lmhead_logits(dev(inp["hidden"]), dev(inp["w"]))
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64)
+
+
+def _bound(inp, dtype):
+    """fp32 accumulation bound over H terms: |err| <= gamma_H * sum_k |h_k w_k| (+ output rounding)."""
+    h = np.abs(oracle.decode(inp["hidden"], dtype))
+    w = np.abs(oracle.decode(inp["w"], dtype))
+    H = h.shape[1]
+    u = 2.0 ** -24
+    return (H * u / (1 - H * u)) * (h @ w.T) + 1e-30
+
+
+@pytest.mark.parametrize("M,H,V,dtype", [(16, 64, 1024, "f32"), (5, 96, 1000, "f32"), (48, 64, 300, "f32"),
+                                         (16, 2688, 4096, "bf16"), (48, 96, 1000, "bf16"),
+                                         (128, 2688, 2048, "bf16"), (64, 2688, 2304, "bf16"),
+                                         (512, 2688, 1024, "bf16"), (100, 288, 777, "bf16"), (1, 32, 256, "bf16")])
+def test_full_compare(M, H, V, dtype):
+    wl = synth.workload(1, B=1, H=H, V=V, dtype=dtype)
+    wl.B, wl.S = 1, M
+    wl.wid = 700 + M + H + V
+    inp = synth.lmhead_inputs(wl)
+    got = _run(inp)
+    ref = oracle.lmhead_logits(inp["hidden"], inp["w"], dtype)
+    err = np.abs(got - ref)
+    assert float(err.max()) <= (ATOL_BF16 if dtype == "bf16" else ATOL_F32)
+    assert np.all(err <= _bound(inp, dtype) + np.abs(ref) * 2.0 ** -24)
+
+
+def test_one_hot_hidden_reads_weight_columns_exactly():
+    wl = synth.workload(1, V=3000, H=256)
+    wl.wid = 801
+    w = synth.lmhead_inputs(wl)["w"]
+    hid = np.zeros((32, 256), np.float32)
+    for m in range(32):
+        hid[m, (m * 7) % 256] = 1.0
+    got = _run(dict(hidden=synth.to_bf16_bits(hid), w=w))
+    for m in range(32):
+        assert np.array_equal(got[m], oracle.decode(w[:, (m * 7) % 256], "bf16"))
+
+
+@pytest.mark.parametrize("wid", [1, 2, 3, 4])
+def test_workload_full_size_sampled(wid):
+    wl = synth.workload(wid)
+    inp = synth.lmhead_inputs(wl)
+    got = _run(inp)
+    g = np.random.default_rng(wid)
+    pairs = [(int(g.integers(wl.M)), int(g.integers(wl.V))) for _ in range(3000)]
+    pairs += [(0, 0), (wl.M - 1, wl.V - 1), (wl.M - 1, 0), (0, wl.V - 1)]
+    ref = oracle.lmhead_entries(inp["hidden"], inp["w"], "bf16", pairs)
+    gv = np.array([got[m, v] for (m, v) in pairs])
+    assert float(np.max(np.abs(gv - ref))) <= ATOL_BF16
+    # one full row against the oracle as well
+    m = wl.M // 2
+    rowref = oracle.decode(inp["w"], "bf16") @ oracle.decode(inp["hidden"][m], "bf16")
+    assert float(np.max(np.abs(got[m] - rowref))) <= ATOL_BF16
+
+
+def test_deterministic():
+    wl = synth.workload(1, V=8192)
+    wl.wid = 802
+    inp = synth.lmhead_inputs(wl)
+    h, w = dev(inp["hidden"]), dev(inp["w"])
+    a = bmd.tt_lmhead_logits(h, w)
+    b = bmd.tt_lmhead_logits(h, w)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
