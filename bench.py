@@ -1,0 +1,309 @@
+"""Benchmark of the TwoTower denoiser block step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1..4] [--no-cpu-baseline]
+
+One step = one pass of the whole hot path over one batch of blocks: block attention for every
+layer, the LM-head product, the synthetic logit spikes (input construction, not the method),
+and confidence unmasking. Steps cycle through the T = 16 steps of a block; at each block
+boundary the block state (tokens, mask bits) is reset from a pristine copy. Inputs are seeded
+synthetic tensors (synth), uploaded to HBM before the timed region.
+
+Prints one JSON line. `value` = denoise block-steps per second (a block-step = one step of one
+block that still had a masked position at the start of the step); committed tokens/s and
+per-kernel rooflines ride along. Per-kernel durations come from HIP events recorded on the
+stream the kernels are launched on, around every call inside the timed region.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "denoise block-steps/s + committed tokens/s; % HBM roofline (attn), % MFMA (LM head)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 MFMA
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "lmhead_w1_traffic.txt")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--workload", type=int, default=1, choices=[1, 2, 3, 4])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-steps", type=int, default=2, help="oracle block-steps in the CPU sample")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="run a 1 GiB device copy first (calibrates HBM byte counters)")
+    return ap.parse_args()
+
+
+def algorithmic(wl):
+    """Algorithmic bytes / flops per call at this workload (attention: one layer). Attention bytes:
+    the context K/V rows read once, Q, the block's K/V, and the output. LM head: W, hidden and
+    the fp32 logits written. Split-K partials are overhead and not counted."""
+    e = 2 if wl.dtype == "bf16" else 4
+    B, S, Hq, Hkv, D, G = wl.B, wl.S, wl.Hq, wl.Hkv, wl.D, wl.G
+    sumP = float(sum(wl.prefixes))
+    attn_bytes = e * (2 * Hkv * sumP * D + 2 * B * S * Hq * D + 2 * B * S * Hkv * D)
+    attn_flops = 4.0 * S * G * D * Hkv * (sumP + B * S)
+    lm_bytes = e * (wl.V * wl.H + wl.M * wl.H) + 4.0 * wl.M * wl.V
+    lm_flops = 2.0 * wl.M * wl.H * wl.V
+    return dict(attn_bytes=attn_bytes, attn_flops=attn_flops, lm_bytes=lm_bytes, lm_flops=lm_flops)
+
+
+def read_traffic(src_hash):
+    """HBM bytes per launch of the LM-head kernel from the committed counter summary, if it was
+    taken on the current kernel source; else None."""
+    try:
+        kv = {}
+        for line in open(PROFILE_TRAFFIC):
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+        if kv.get("source_sha256") != src_hash:
+            return None
+        return float(kv["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("lmhead.hip", "common.h"):
+        h.update(open(os.path.join(ROOT, "block_mask_diffusion_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
+
+
+def cpu_baseline(wl, host, steps):
+    """The oracle, as it stands, on a bounded sample: `steps` block-steps of sequence 0
+    (every layer's attention for its kv heads, its S LM-head rows, its unmask)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        blas_threads = 1
+    S = wl.S
+    layers = []
+    for inp in host["attn"]:
+        a, n = int(inp["ctx_start"][0]), int(inp["ctx_len"][0])
+        layers.append(dict(q=inp["q"][:1], k_blk=inp["k_blk"][:1], v_blk=inp["v_blk"][:1],
+                           k_ctx=inp["k_ctx"][:, a:a + n], v_ctx=inp["v_ctx"][:, a:a + n],
+                           ctx_start=np.array([0], np.int32), ctx_len=np.array([n], np.int32),
+                           scale=inp["scale"]))
+    tokens, bits = host["tokens"][:1].copy(), host["bits"][:1].copy()
+    t0 = time.perf_counter()
+    for step in range(steps):
+        r = oracle.denoise_step(layers, host["hidden"][:S], host["w"], wl.dtype, host["spike_tok"][:S],
+                                host["spike_val"][:S], tokens, bits, S, step % wl.T, wl.T, wl.gamma, wl.mask_id)
+        tokens, bits = r["tokens"], r["mask_bits"]
+    dt = time.perf_counter() - t0
+    return {"value": steps / dt, "unit": "block-steps/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"{steps} block-steps of sequence 0 (all {len(layers)} attention layer(s), "
+                      f"{S} LM-head rows, unmask) with numpy fp64; host has {os.cpu_count()} CPUs, "
+                      f"BLAS threads {blas_threads}",
+            "seconds": dt}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the path is built and measured "
+              "on a single MI355X", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import synth
+    import block_mask_diffusion_amd as bmd
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    wl = synth.workload(args.workload)
+    dev = torch.device("cuda")
+
+    def up(x):
+        if x.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev).view(torch.bfloat16)
+        if x.dtype == np.uint64:
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int64)).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    want_cpu = not args.no_cpu_baseline
+    t_gen = time.perf_counter()
+    host = {"attn": []}
+    attn_d = []
+    for layer in range(wl.layers):
+        inp = synth.attn_inputs(wl, layer)
+        attn_d.append({k: (up(v) if isinstance(v, np.ndarray) else v) for k, v in inp.items()})
+        if want_cpu:
+            host["attn"].append(inp)
+        del inp
+    lm = synth.lmhead_inputs(wl)
+    hidden_d, w_d = up(lm["hidden"]), up(lm["w"])
+    sp = synth.spikes(wl)
+    st0 = synth.initial_state(wl)
+    if want_cpu:
+        host.update(hidden=lm["hidden"], w=lm["w"], spike_tok=sp["tok"], spike_val=sp["val"],
+                    tokens=st0["tokens"], bits=st0["mask_bits"])
+    del lm
+    gen_s = time.perf_counter() - t_gen
+
+    # synthetic spikes: one entry per logits row, added with a single index_add_ on the flat view
+    spk_idx_d = torch.from_numpy(np.arange(wl.M, dtype=np.int64) * wl.V + sp["tok"]).to(dev)
+    spk_val_d = torch.from_numpy(sp["val"]).to(dev)
+    tok0_d, bits0_d = up(st0["tokens"]), up(st0["mask_bits"])
+    tokens_d, bits_d = tok0_d.clone(), bits0_d.clone()
+    logits_d = torch.empty((wl.M, wl.V), dtype=torch.float32, device=dev)
+    attn_out = [torch.empty_like(a["q"]) for a in attn_d]
+    K, Wm = args.steps, args.warmup
+    nm_hist = torch.zeros((K, wl.B), dtype=torch.int32, device=dev)
+    nm_scratch = torch.zeros((wl.B,), dtype=torch.int32, device=dev)
+    ws_attn = torch.empty(bmd.workspace_bytes("tt_block_attn", B=wl.B, S=wl.S, Hq=wl.Hq, Hkv=wl.Hkv, D=wl.D,
+                                              ctx_rows=wl.ctx_rows, max_prefix=wl.max_prefix),
+                          dtype=torch.uint8, device=dev)
+    ws_um = torch.empty(max(256, bmd.workspace_bytes("tt_confidence_unmask", B=wl.B, S=wl.S, V=wl.V)),
+                        dtype=torch.uint8, device=dev)
+
+    if args.copy_calib:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    stream = torch.cuda.current_stream()
+
+    def step(t, nm_out, ev=None):
+        s = t % wl.T
+        if s == 0:
+            tokens_d.copy_(tok0_d)
+            bits_d.copy_(bits0_d)
+        if ev is not None:
+            ev[0].record(stream)
+        for a, o in zip(attn_d, attn_out):
+            bmd.tt_block_attn(a["q"], a["k_blk"], a["v_blk"], a["k_ctx"], a["v_ctx"], a["ctx_start"],
+                              a["ctx_len"], max_prefix=wl.max_prefix, softmax_scale=a["scale"], out=o,
+                              workspace=ws_attn)
+        if ev is not None:
+            ev[1].record(stream)
+        bmd.tt_lmhead_logits(hidden_d, w_d, logits_d)
+        if ev is not None:
+            ev[2].record(stream)
+        logits_d.view(-1).index_add_(0, spk_idx_d, spk_val_d)  # synthetic spikes
+        if ev is not None:
+            ev[3].record(stream)
+        bmd.tt_confidence_unmask(logits_d, tokens_d, bits_d, nm_out, s, wl.T, wl.gamma, wl.mask_id,
+                                 workspace=ws_um)
+        if ev is not None:
+            ev[4].record(stream)
+
+    for t in range(Wm):
+        step(t, nm_scratch)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for t in range(K):
+        step(t, nm_hist[t], evs[t])
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    total_ms = start.elapsed_time(end)
+
+    t_attn = sum(e[0].elapsed_time(e[1]) for e in evs) / K
+    t_lm = sum(e[1].elapsed_time(e[2]) for e in evs) / K
+    t_spk = sum(e[2].elapsed_time(e[3]) for e in evs) / K
+    t_um = sum(e[3].elapsed_time(e[4]) for e in evs) / K
+
+    # block-steps and commits from the per-step n_masked record
+    nm = nm_hist.cpu().numpy()
+    init_masked = np.array([bin(int(b)).count("1") for b in st0["mask_bits"]])
+    block_steps, commits, masked_rows = 0, 0, 0
+    for t in range(K):
+        start_masked = init_masked if t % wl.T == 0 else nm[t - 1]
+        block_steps += int(np.sum(start_masked > 0))
+        commits += int(np.sum(start_masked - nm[t]))
+        masked_rows += int(np.sum(start_masked))
+    sec = total_ms / 1e3
+    alg = algorithmic(wl)
+    lm_gbs = alg["lm_bytes"] / (t_lm / 1e3) / 1e9
+    t_attn_call = t_attn / wl.layers  # ms per tt_block_attn call (one layer)
+    attn_gbs = alg["attn_bytes"] / (t_attn_call / 1e3) / 1e9
+    um_bytes = 4.0 * wl.V * masked_rows / K
+    um_gbs = um_bytes / (t_um / 1e3) / 1e9
+    lm_tfs = alg["lm_flops"] / (t_lm / 1e3) / 1e12
+    attn_tfs = alg["attn_flops"] / (t_attn_call / 1e3) / 1e12
+    # attainable LM-head rate: min(MFMA peak, arithmetic intensity x HBM peak)
+    lm_attain_tfs = min(MFMA_BF16_PEAK_TFS, alg["lm_flops"] / alg["lm_bytes"] * HBM_PEAK_GBS / 1e3)
+
+    times = {"attn": t_attn, "lmhead": t_lm, "unmask": t_um}
+    dominant = max(times, key=times.get)
+    if dominant == "lmhead":
+        traffic = read_traffic(source_hash())
+        roof = {"kernel": "lmhead_lds_kernel (tt_lmhead_logits)", "bound": "hbm", "achieved": round(lm_gbs, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(lm_gbs / HBM_PEAK_GBS, 4),
+                "traffic": traffic, "algorithmic_bytes": alg["lm_bytes"], "avg_launch_us": round(t_lm * 1e3, 2)}
+    elif dominant == "attn":
+        roof = {"kernel": "attn_partial + attn_combine (tt_block_attn)", "bound": "hbm",
+                "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "algorithmic_bytes": alg["attn_bytes"], "avg_launch_us": round(t_attn_call * 1e3, 2)}
+    else:
+        roof = {"kernel": "unmask (tt_confidence_unmask)", "bound": "hbm", "achieved": round(um_gbs, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(um_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "algorithmic_bytes": um_bytes, "avg_launch_us": round(t_um * 1e3, 2)}
+
+    cpu = None
+    if want_cpu:
+        cpu = cpu_baseline(wl, host, args.cpu_steps)
+        cpu.pop("seconds", None)
+
+    out = {
+        "metric": METRIC,
+        "value": round(block_steps / sec, 2),
+        "unit": "block-steps/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wm,
+        "ms_per_step": round(total_ms / K, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded normal Q/K/V, hidden, W~N(0,0.02^2), uniform logit spikes)",
+        "config": {"workload": f"w{wl.wid}: {wl.name}", "batch": wl.B, "block": wl.S, "prefix_max": wl.max_prefix,
+                   "prefix_sum": wl.ctx_rows, "q_heads": wl.Hq, "kv_heads": wl.Hkv, "head_dim": wl.D,
+                   "hidden": wl.H, "vocab": wl.V, "layers": wl.layers, "steps_per_block": wl.T,
+                   "gamma": wl.gamma, "mask_id": wl.mask_id},
+        "committed_tokens_per_s": round(commits / sec, 2),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernels": {
+            "attn": {"us_per_layer": round(t_attn / wl.layers * 1e3, 2), "GB_s": round(attn_gbs, 1),
+                     "hbm_frac": round(attn_gbs / HBM_PEAK_GBS, 4), "TFLOP_s": round(attn_tfs, 1),
+                     "mfma_frac": round(attn_tfs / MFMA_BF16_PEAK_TFS, 4)},
+            "lmhead": {"us": round(t_lm * 1e3, 2), "GB_s": round(lm_gbs, 1), "hbm_frac": round(lm_gbs / HBM_PEAK_GBS, 4),
+                       "TFLOP_s": round(lm_tfs, 2), "mfma_frac": round(lm_tfs / MFMA_BF16_PEAK_TFS, 4),
+                       "attainable_frac": round(lm_tfs / lm_attain_tfs, 4)},
+            "unmask": {"us": round(t_um * 1e3, 2), "GB_s": round(um_gbs, 1), "hbm_frac": round(um_gbs / HBM_PEAK_GBS, 4)},
+            "spikes_us": round(t_spk * 1e3, 2),
+        },
+        "wall_s_timed": round(wall, 3),
+        "input_gen_s": round(gen_s, 1),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

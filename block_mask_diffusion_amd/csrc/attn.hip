@@ -11,25 +11,33 @@
 // in slot w + u of the workspace, which attn_combine merges in a fixed order. Slot w + u is
 // injective because walking the pieces in order raises w or u (or both) at every boundary.
 //
-// Inside a workgroup (8 waves, one 32-row query tile each): each K/V stage of KC keys is staged once in LDS and shared by all
-// S*G query rows (up to 256), so every key byte is read from HBM once. Scores are computed
-// transposed, S^T = K Q^T, on 32x32 MFMA tiles: the result layout gives each lane one query row
-// (column lane%32) and 16 keys, so the row max and sum need one cross-half exchange only. The
-// exponentials are written back into the same registers and used directly as the B operand of
-// O^T = V^T P^T; the reduction order over keys inside a stage is a fixed permutation, applied to
-// V when it is written transposed into LDS.
+// Inside a workgroup (4 waves, two 32-row query tiles each): K/V stages of KC keys go straight from
+// HBM into an LDS ring of NBUF stages (direct global->LDS loads, three stages in flight) and are
+// shared by all S*G query rows (up to 256), so every key byte is read from HBM once. Scores are
+// computed transposed, S^T = K Q^T, on 32x32 MFMA tiles: the result layout gives each lane one
+// query row (column lane%32) and 16 keys, so the row max and sum need one cross-half exchange
+// only. The exponentials are written back into the same registers and used directly as the B
+// operand of O^T = V^T P^T; the V^T operand is read from the row-major V stage with transposing
+// LDS reads, in the key order of the score registers.
 #include "common.h"
 
 namespace {
 
-constexpr int AT_THREADS = 512;
+#ifndef TT_AT_TPW
+#define TT_AT_TPW 1
+#endif
+#ifndef TT_AT_PRIO
+#define TT_AT_PRIO 1
+#endif
+constexpr int TPW = TT_AT_TPW;  // query tiles per wave (each K/V fragment read feeds TPW MFMAs)
+constexpr int AT_THREADS = 512 / TPW;
 constexpr int AT_WAVES = AT_THREADS / TT_WAVE;
-constexpr int KC = 64;          // keys per LDS stage
 constexpr int QT = 32;          // query rows per MFMA tile
-constexpr int MAX_ROWS = 256;   // S*G limit: 8 tiles, one per wave
-constexpr int NT = MAX_ROWS / QT / AT_WAVES;
+constexpr int MAX_ROWS = 256;   // S*G limit: 8 tiles
 constexpr int AT_MAX_B = 1024;  // sequences handled by the in-workgroup prefix scan
 constexpr float LOG2E = 1.4426950408889634f;
+static_assert(MAX_ROWS == QT * TPW * AT_WAVES, "8 query tiles per workgroup");
+constexpr float RESCALE_LOG2 = 8.f;  // lazy-rescale threshold (log2 units)
 
 template <typename T>
 struct Mf;
@@ -38,15 +46,13 @@ template <>
 struct Mf<bf16> {
   static constexpr int KS = 16;   // reduction depth of v_mfma_f32_32x32x16_bf16
   static constexpr int EPL = 8;   // operand elements per lane
-  static constexpr int VPAD = 8;  // Vt row padding (elements); keeps rows 16-byte aligned
   typedef bf16x8 frag;
   __device__ static __forceinline__ f32x16 mma(frag a, frag b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
-  // Position of key `k` (within a stage) in the transposed V rows. The score registers j=8u..8u+7
-  // of lane half h hold keys 16u + 8(j%8/4) + 4h + j%4; MFMA u consumes them as reduction
-  // indices 16u + 8h + j%8, so the position swaps key bits 2 and 3.
-  __device__ static __forceinline__ int vpos(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
+  // P^T operand of MFMA u: score registers 8u..8u+7, rounded to bf16. Register j of lane half h
+  // holds key 8(j/4) + 4h + j%4 of the sub-tile, i.e. keys 16u + 4h + {0..3} and 16u + 8 + 4h +
+  // {0..3}; the V^T operand is read in the same key order.
   __device__ static __forceinline__ frag pfrag(const f32x16& p, int u) {
     frag f;
 #pragma unroll
@@ -59,25 +65,47 @@ template <>
 struct Mf<float> {
   static constexpr int KS = 2;    // v_mfma_f32_32x32x2f32
   static constexpr int EPL = 1;
-  static constexpr int VPAD = 1;  // odd row length: conflict-free column reads
   typedef float frag;
   __device__ static __forceinline__ f32x16 mma(frag a, frag b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
   }
-  // register j = u of lane half h holds key 8(u/4) + 4h + u%4 and feeds reduction index 2u + h
-  __device__ static __forceinline__ int vpos(int k) {
-    return (k & ~7) | ((k & 3) << 1) | ((k >> 2) & 1);
-  }
+  // register u of lane half h holds key 8(u/4) + 4h + u%4 and feeds reduction slot 2u + h
   __device__ static __forceinline__ frag pfrag(const f32x16& p, int u) { return p[u]; }
 };
 
+// Stage geometry: KC keys per stage (64 for bf16, 32 for fp32), K and V stored row-major in an
+// LDS ring of NBUF stages, written by direct global->LDS loads.
+template <typename T>
+constexpr int kc_of() { return sizeof(T) == 2 ? 64 : 32; }
+constexpr int NBUF = 4;
+
 template <typename T, int D>
-struct Smem {
-  static constexpr int KPAD = 16 / (int)sizeof(T);
-  static constexpr int KROW = D + KPAD;
-  static constexpr int VROW = KC + Mf<T>::VPAD;
-  T k[2][KC][KROW];
-  T vt[2][D][VROW];
+struct Geo {
+  static constexpr int KC = kc_of<T>();
+  static constexpr int RB = D * (int)sizeof(T);        // bytes per key row
+  static constexpr int GPR = RB / 16;                  // 16-byte granules per row
+  static constexpr int RPC = 1024 / RB;                // rows per 1 KiB load chunk (64 lanes x 16 B)
+  static constexpr int NCH = KC * RB / 1024;           // chunks per stage, for K and for V
+  static constexpr int STAGE = KC * RB;                // bytes of K (or V) per stage
+  static constexpr int DPW = 2 * NCH / AT_WAVES;       // load instructions per wave per stage
+  static constexpr int RPW = RB >= 256 ? 1 : 256 / RB; // rows per 256-byte bank window
+  static constexpr int GMASK = GPR - 1 < 15 ? GPR - 1 : 15;
+  static_assert(NCH % AT_WAVES == 0, "chunks split over the waves");
+  // XOR swizzle of the 16-byte granules of row r (an involution, applied on the load side):
+  // K rows read 32 at a time at one logical granule -> spread over all banks;
+  // V rows read 8 at a time by the transposing reads -> at most 2-way conflicts.
+  __device__ static __forceinline__ int fk(int r) { return (r / RPW) & GMASK; }
+  __device__ static __forceinline__ int fv(int r) {
+    if constexpr (sizeof(T) == 2 && D == 128) return 4 * (r & 3);
+    else if constexpr (sizeof(T) == 2 && D == 64) return 4 * ((r >> 1) & 1);
+    else return fk(r);
+  }
+};
+
+template <typename T, int D>
+struct alignas(16) Ring {
+  unsigned char k[NBUF][Geo<T, D>::STAGE];
+  unsigned char v[NBUF][Geo<T, D>::STAGE];
 };
 
 struct Scan {
@@ -138,28 +166,35 @@ struct Args {
   float c;  // softmax_scale * log2(e)
 };
 
+template <int N>
+__device__ __forceinline__ void wait_vmem() {  // this wave's oldest outstanding VMEM ops, all but N
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
+
 template <typename T, int D>
 __global__ __launch_bounds__(AT_THREADS, 1) void attn_partial(Args<T, D> A) {
   typedef Mf<T> MF;
+  typedef Geo<T, D> GE;
   typedef typename MF::frag frag;
-  constexpr int KS = MF::KS, EPL = MF::EPL;
-  constexpr int EV = 16 / (int)sizeof(T);        // elements per 16-byte vector
-  constexpr int NVR = D / EV;                    // vectors per key row
-  constexpr int NVEC = KC * NVR / AT_THREADS;    // vectors per thread per stage (K, and V)
-  static_assert(KC * NVR % AT_THREADS == 0, "stage split");
+  constexpr int KS = MF::KS, EPL = MF::EPL, KC = GE::KC, RB = GE::RB, GPR = GE::GPR;
+  constexpr int SPS = KC / 32;                  // 32-key sub-tiles per stage
+  constexpr int CPW = GE::NCH / AT_WAVES;       // K (and V) chunks per wave per stage
 
-  __shared__ Smem<T, D> sm;
+  __shared__ Ring<T, D> ring;
   __shared__ Scan sc;
 
   const int tid = threadIdx.x;
   const int lane = tid & (TT_WAVE - 1);
-  const int wave = tid / TT_WAVE;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / TT_WAVE);  // uniform per wave
   const int l32 = lane & 31;
   const int hh2 = lane >> 5;  // lane half
   const int w = blockIdx.x;
   const int G = A.Hq / A.Hkv;
   const int R = A.S * G;
   const int U = A.B * A.Hkv;
+  const bool active = wave * TPW * QT < R;  // this wave owns query rows [32*TPW*wave, +32*TPW)
 
   scan_lengths(sc, A.ctx_len, A.B, A.S);
   const int64_t Ttot = (int64_t)A.Hkv * sc.pb[A.B];
@@ -188,216 +223,262 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_partial(Args<T, D> A) {
     const int ke = (int)min((int64_t)N, hi - Ou);
     const bool whole = (ka == 0 && ke == N);
     const int P = N - A.S;
-    const int64_t cstart = A.ctx_start[bb];
+    const T* kctx = A.kc + ((size_t)g * A.ctx_rows + A.ctx_start[bb]) * D;  // row 0 of this unit
+    const T* vctx = A.vc + ((size_t)g * A.ctx_rows + A.ctx_start[bb]) * D;
+    const size_t blk_stride = (size_t)A.Hkv * D;                             // between block rows
+    const T* kblk = A.kb + ((size_t)bb * A.S * A.Hkv + g) * D;
+    const T* vblk = A.vb + ((size_t)bb * A.S * A.Hkv + g) * D;
 
-    // ---- query fragments (B operand of S^T = K Q^T): lane holds row 32t + l32
-    frag qf[NT][D / KS];
+    // ---- query fragments (B operand of S^T = K Q^T): lane holds row `row`
+    frag qf[TPW][D / KS];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int tile = wave + AT_WAVES * nt;
-      const int row = tile * QT + l32;
-      const bool ok = row < R;
+    for (int t = 0; t < TPW; ++t) {
+      const int row = (wave * TPW + t) * QT + l32;
+      const bool ok = active && row < R;
       const int s = ok ? row / G : 0, hq = ok ? g * G + row % G : 0;
       const T* qp = A.q + (((size_t)bb * A.S + s) * A.Hq + hq) * D;
 #pragma unroll
       for (int ks = 0; ks < D / KS; ++ks) {
         if (ok) {
-          if constexpr (EPL == 8) qf[nt][ks] = *reinterpret_cast<const frag*>(qp + KS * ks + EPL * hh2);
-          else qf[nt][ks] = qp[KS * ks + hh2];
+          if constexpr (EPL == 8) qf[t][ks] = *reinterpret_cast<const frag*>(qp + KS * ks + EPL * hh2);
+          else qf[t][ks] = qp[KS * ks + hh2];
         } else {
-          if constexpr (EPL == 8) { for (int i = 0; i < 8; ++i) qf[nt][ks][i] = (bf16)0.f; }
-          else qf[nt][ks] = 0.f;
+          if constexpr (EPL == 8) { for (int i = 0; i < 8; ++i) qf[t][ks][i] = (bf16)0.f; }
+          else qf[t][ks] = 0.f;
         }
       }
     }
 
-    f32x16 o[NT][D / 32];
-    float mrun[NT], lrun[NT];
+    f32x16 o[TPW][D / 32];
+    float mrun[TPW], lrun[TPW];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      mrun[nt] = -INFINITY;
-      lrun[nt] = 0.f;
+    for (int t = 0; t < TPW; ++t) {
+      mrun[t] = -INFINITY;
+      lrun[t] = 0.f;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) o[nt][dt][j] = 0.f;
+        for (int j = 0; j < 16; ++j) o[t][dt][j] = 0.f;
     }
 
-    // ---- stage loader: global -> registers -> LDS
-    u32x4 kreg[NVEC], vreg[NVEC];
-    auto row_ptr = [&](const T* ctx, const T* blk, int key) -> const T* {
-      return key < P ? ctx + ((size_t)g * A.ctx_rows + cstart + key) * D
-                     : blk + (((size_t)bb * A.S + (key - P)) * A.Hkv + g) * D;
-    };
-    auto gload = [&](int k0) {
+    // ---- stage loads: global -> LDS directly. Chunk c of a stage holds rows [c*RPC, c*RPC+RPC);
+    // lane i writes LDS bytes [16i, 16i+16) of the chunk = granule slot i%GPR of row i/GPR, which
+    // holds logical granule slot ^ f(row). Keys past the piece end re-read its last key (their
+    // scores are masked and their probabilities are exactly 0).
+    const int nkeys = ke - ka;
+    auto issue_stage = [&](int st) {
+      const int buf = st % NBUF;
+      const int k0 = ka + st * KC;
 #pragma unroll
-      for (int i = 0; i < NVEC; ++i) {
-        const int v = tid + AT_THREADS * i;
-        {  // K: consecutive threads walk a key row (coalesced rows)
-          const int key = v / NVR, piece = v % NVR;
-          const int kk = k0 + key;
-          kreg[i] = (kk < ke) ? *reinterpret_cast<const u32x4*>(row_ptr(A.kc, A.kb, kk) + piece * EV)
-                              : u32x4{0u, 0u, 0u, 0u};
-        }
-        {  // V: consecutive threads walk keys (conflict-free transposed LDS writes)
-          const int key = v % KC, piece = v / KC;
-          const int kk = k0 + key;
-          vreg[i] = (kk < ke) ? *reinterpret_cast<const u32x4*>(row_ptr(A.vc, A.vb, kk) + piece * EV)
-                              : u32x4{0u, 0u, 0u, 0u};
+      for (int c = 0; c < CPW; ++c) {
+        const int chunk = wave * CPW + c;
+        const int r = chunk * GE::RPC + lane / GPR, slot = lane % GPR;
+        int key = k0 + r;
+        key = key < ke ? key : ke - 1;
+        const int gk = slot ^ GE::fk(r), gv = slot ^ GE::fv(r);
+        const T* kp = key < P ? kctx + (size_t)key * D : kblk + (size_t)(key - P) * blk_stride;
+        const T* vp = key < P ? vctx + (size_t)key * D : vblk + (size_t)(key - P) * blk_stride;
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const unsigned char*>(kp) + 16 * gk,
+                                         LDS_PTR(void, &ring.k[buf][chunk * 1024]), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const unsigned char*>(vp) + 16 * gv,
+                                         LDS_PTR(void, &ring.v[buf][chunk * 1024]), 16, 0, 0);
+      }
+    };
+    // stage st resident: wait for this wave's loads of stage st (the later stages stay in flight),
+    // then a barrier so every wave's loads of stage st are in LDS
+    auto stage_ready = [&](int st, int nst) {
+      const int later = min(nst - 1, st + NBUF - 2) - st;  // stages issued after st
+      if (later >= 2) wait_vmem<2 * GE::DPW>();
+      else if (later == 1) wait_vmem<GE::DPW>();
+      else wait_vmem<0>();
+      tt_lds_barrier();
+    };
+
+    auto kread = [&](const unsigned char* kb_, int kt, frag (&kf)[D / KS]) {
+      const int r = kt * 32 + l32;
+      const unsigned char* rp = kb_ + r * RB;
+      const int f = GE::fk(r);
+#pragma unroll
+      for (int ks = 0; ks < D / KS; ++ks) {
+        if constexpr (EPL == 8) {
+          kf[ks] = *reinterpret_cast<const frag*>(rp + 16 * ((2 * ks + hh2) ^ f));
+        } else {
+          const int d = KS * ks + hh2;
+          kf[ks] = *reinterpret_cast<const float*>(rp + 16 * ((d >> 2) ^ f) + 4 * (d & 3));
         }
       }
     };
-    auto swrite = [&](int buf) {
+    auto qk = [&](const frag (&kf)[D / KS], f32x16 (&acc)[TPW]) {
 #pragma unroll
-      for (int i = 0; i < NVEC; ++i) {
-        const int v = tid + AT_THREADS * i;
-        {
-          const int key = v / NVR, piece = v % NVR;
-          *reinterpret_cast<u32x4*>(&sm.k[buf][key][piece * EV]) = kreg[i];
-        }
-        {
-          const int key = v % KC, piece = v / KC;
-          const int pos = MF::vpos(key);
-          const T* e = reinterpret_cast<const T*>(&vreg[i]);
+      for (int t = 0; t < TPW; ++t)
 #pragma unroll
-          for (int x = 0; x < EV; ++x) sm.vt[buf][piece * EV + x][pos] = e[x];
+        for (int j = 0; j < 16; ++j) acc[t][j] = 0.f;
+      if (TT_AT_PRIO) __builtin_amdgcn_s_setprio(2);  // MFMA phase: let this wave issue first
+      if constexpr (TPW == 1) {
+        // two accumulation chains (even / odd k-steps) so consecutive MFMAs are independent
+        f32x16 acc2;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc2[j] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < D / KS; ks += 2) {
+          acc[0] = MF::mma(kf[ks], qf[0][ks], acc[0]);
+          acc2 = MF::mma(kf[ks + 1], qf[0][ks + 1], acc2);
         }
+        acc[0] += acc2;
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < D / KS; ++ks)
+#pragma unroll
+          for (int t = 0; t < TPW; ++t) acc[t] = MF::mma(kf[ks], qf[t][ks], acc[t]);
+      }
+      if (TT_AT_PRIO) __builtin_amdgcn_s_setprio(0);
+    };
+    // V^T fragment of MFMA uu / d-tile dt: keys of the P registers 8uu..8uu+7 of this lane half
+    auto vfrag = [&](const unsigned char* vb_, int kt, int uu, int dt) -> frag {
+      if constexpr (EPL == 8) {
+        // two transposing reads: 16-lane group G, lane j of it gets V[kb + e][d0 + j], e = 0..3,
+        // when source lane j points at V[kb + j/4][d0 + 4*(j%4)]
+        const int G4 = lane >> 4, j = lane & 15;
+        const int d = dt * 32 + 16 * (G4 & 1) + 4 * (j & 3);
+        frag f;
+#pragma unroll
+        for (int rd = 0; rd < 2; ++rd) {
+          const int r = kt * 32 + 16 * uu + 4 * (G4 >> 1) + 8 * rd + (j >> 2);
+          const unsigned char* p = vb_ + r * RB + 16 * ((d >> 3) ^ GE::fv(r)) + 2 * (d & 7);
+          typedef short s16x4 __attribute__((ext_vector_type(4)));
+          s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, p));
+          bf16x4 y = __builtin_bit_cast(bf16x4, x);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) f[4 * rd + e] = y[e];
+        }
+        return f;
+      } else {
+        // fp32: register uu of lane half h holds key 8(uu/4) + 4h + uu%4
+        const int r = kt * 32 + 8 * (uu >> 2) + 4 * hh2 + (uu & 3);
+        const int d = dt * 32 + l32;
+        return *reinterpret_cast<const float*>(vb_ + r * RB + 16 * ((d >> 2) ^ GE::fv(r)) + 4 * (d & 3));
       }
     };
 
-    const int nst = (ke - ka + KC - 1) / KC;
-    gload(ka);
-    __syncthreads();  // previous piece's readers are done with both buffers
-    swrite(0);
-    __syncthreads();
+    const int nst = (nkeys + KC - 1) / KC;
+    wait_vmem<0>();   // the previous piece's partial stores; the load counting below starts clean
+    __syncthreads();  // previous piece's readers are done with the ring
+#pragma unroll
+    for (int st = 0; st < NBUF - 1; ++st)
+      if (st < nst) issue_stage(st);
 
     for (int st = 0; st < nst; ++st) {
-      const int buf = st & 1;
-      const int k0 = ka + st * KC;
-      const int nvalid = min(KC, ke - k0);
-      if (st + 1 < nst) gload(k0 + KC);
-
-      // The stage is consumed as KC/32 sub-tiles of 32 keys, each a full online-softmax update,
-      // which keeps only 32 keys of scores live per query tile.
+      stage_ready(st, nst);                                  // B_st
+      if (st + NBUF - 1 < nst) issue_stage(st + NBUF - 1);   // into the buffer of stage st-1
+      const unsigned char* kbuf = ring.k[st % NBUF];
+      const unsigned char* vbuf = ring.v[st % NBUF];
+      if (active) {
 #pragma unroll
-      for (int kt = 0; kt < KC / 32; ++kt) {
-        // ---- S^T tile: 32 keys on rows, query rows on columns
-        f32x16 sacc[NT];
+        for (int kt = 0; kt < SPS; ++kt) {
+          const int kvalid = nkeys - st * KC - kt * 32;  // keys of this sub-tile that exist
+          if (kvalid > 0) {
+            frag kf[D / KS];
+            kread(kbuf, kt, kf);
+            f32x16 sacc[TPW];
+            qk(kf, sacc);
+            frag pf[TPW][32 / KS];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
+            for (int t = 0; t < TPW; ++t) {
+              if (kvalid < 32) {
 #pragma unroll
-          for (int j = 0; j < 16; ++j) sacc[nt][j] = 0.f;
+                for (int j = 0; j < 16; ++j)
+                  if (8 * (j >> 2) + 4 * hh2 + (j & 3) >= kvalid) sacc[t][j] = -INFINITY;
+              }
+              float mx = fmaxf(fmaxf(sacc[t][0], sacc[t][1]), sacc[t][2]);
 #pragma unroll
-        for (int ks = 0; ks < D / KS; ++ks) {
-          frag a;
-          if constexpr (EPL == 8) a = *reinterpret_cast<const frag*>(&sm.k[buf][kt * 32 + l32][KS * ks + EPL * hh2]);
-          else a = sm.k[buf][kt * 32 + l32][KS * ks + hh2];
+              for (int j = 3; j < 15; j += 2) mx = fmaxf(fmaxf(mx, sacc[t][j]), sacc[t][j + 1]);
+              mx = fmaxf(mx, sacc[t][15]);
+              mx = fmaxf(mx, tt_shfl_xor(mx, 32));
+              // Lazy rescale: the reference max only moves when a row's max grows by more than
+              // 2^8 in the exponent; exponentials stay <= 256 and the final normalisation is exact.
+              if (__ballot((mx - mrun[t]) * A.c > RESCALE_LOG2)) {
+                const float mnew = fmaxf(mrun[t], mx);
+                const float alpha = tt_exp2((mrun[t] - mnew) * A.c);  // 0 on the first update
+                lrun[t] *= alpha;
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt)
-            if ((wave + AT_WAVES * nt) * QT < R) sacc[nt] = MF::mma(a, qf[nt][ks], sacc[nt]);
-        }
-
-        // ---- online softmax (base 2; raw-score max, scale folded into the exponent)
-        const int kvalid = nvalid - kt * 32;  // keys of this sub-tile that exist
+                for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          if ((wave + AT_WAVES * nt) * QT >= R) continue;
-          float mx = -INFINITY;
+                  for (int j = 0; j < 16; ++j) o[t][dt][j] *= alpha;
+                mrun[t] = mnew;
+              }
+              const float mc = mrun[t] * A.c;
+              float ls = 0.f;
 #pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int key = 8 * (j >> 2) + 4 * hh2 + (j & 3);
-            if (key >= kvalid) sacc[nt][j] = -INFINITY;
-            mx = fmaxf(mx, sacc[nt][j]);
-          }
-          mx = fmaxf(mx, tt_shfl_xor(mx, 32));
-          const float mnew = fmaxf(mrun[nt], mx);
-          if (__ballot(mnew > mrun[nt])) {
-            const float alpha = tt_exp2((mrun[nt] - mnew) * A.c);  // 0 on the first update
-            lrun[nt] *= alpha;
+              for (int j = 0; j < 16; ++j) {
+                const float p = tt_exp2(fmaf(sacc[t][j], A.c, -mc));
+                sacc[t][j] = p;
+                ls += p;
+              }
+              lrun[t] += ls;
 #pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt)
+              for (int uu = 0; uu < 32 / KS; ++uu) pf[t][uu] = MF::pfrag(sacc[t], uu);
+            }
+            if (TT_AT_PRIO) __builtin_amdgcn_s_setprio(2);
 #pragma unroll
-              for (int j = 0; j < 16; ++j) o[nt][dt][j] *= alpha;
-            mrun[nt] = mnew;
-          }
-          const float mc = mnew * A.c;
-          float ls = 0.f;
+            for (int dt = 0; dt < D / 32; ++dt) {
+              frag va[32 / KS];
 #pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const float p = tt_exp2(fmaf(sacc[nt][j], A.c, -mc));
-            sacc[nt][j] = p;
-            ls += p;
-          }
-          lrun[nt] += ls;
-        }
-
-        // ---- O^T += V^T P^T
-        frag pf[NT][32 / KS];
+              for (int uu = 0; uu < 32 / KS; ++uu) va[uu] = vfrag(vbuf, kt, uu, dt);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
+              for (int uu = 0; uu < 32 / KS; ++uu)
 #pragma unroll
-          for (int uu = 0; uu < 32 / KS; ++uu) pf[nt][uu] = MF::pfrag(sacc[nt], uu);
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-#pragma unroll
-          for (int uu = 0; uu < 32 / KS; ++uu) {
-            frag a;
-            if constexpr (EPL == 8) a = *reinterpret_cast<const frag*>(&sm.vt[buf][dt * 32 + l32][kt * 32 + KS * uu + EPL * hh2]);
-            else a = sm.vt[buf][dt * 32 + l32][kt * 32 + KS * uu + hh2];
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-              if ((wave + AT_WAVES * nt) * QT < R) o[nt][dt] = MF::mma(a, pf[nt][uu], o[nt][dt]);
+                for (int t = 0; t < TPW; ++t) o[t][dt] = MF::mma(va[uu], pf[t][uu], o[t][dt]);
+            }
+            if (TT_AT_PRIO) __builtin_amdgcn_s_setprio(0);
           }
         }
       }
-
-      if (st + 1 < nst) swrite(buf ^ 1);
-      __syncthreads();
     }
 
     // ---- epilogue: direct normalised output, or an fp32 partial in slot w + u
-    const size_t slot = (size_t)w + u;
+    if (active) {
+      const size_t slot = (size_t)w + u;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int tile = wave + AT_WAVES * nt;
-      if (tile * QT >= R) continue;
-      const float ltot = lrun[nt] + tt_shfl_xor(lrun[nt], 32);
-      const int row = tile * QT + l32;
-      if (row >= R) continue;
-      if (whole) {
-        const int s = row / G, hq = g * G + row % G;
-        T* op = A.out + (((size_t)bb * A.S + s) * A.Hq + hq) * D;
-        const float inv = 1.f / ltot;
+      for (int t = 0; t < TPW; ++t) {
+        const float ltot = lrun[t] + tt_shfl_xor(lrun[t], 32);
+        const int row = (wave * TPW + t) * QT + l32;
+        if (row < R) {
+          if (whole) {
+            const int s = row / G, hq = g * G + row % G;
+            T* op = A.out + (((size_t)bb * A.S + s) * A.Hq + hq) * D;
+            const float inv = 1.f / ltot;
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
+            for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-          for (int jg = 0; jg < 4; ++jg) {
-            const int d = dt * 32 + 8 * jg + 4 * hh2;
-            if constexpr (sizeof(T) == 2) {
-              bf16x4 v;
+              for (int jg = 0; jg < 4; ++jg) {
+                const int d = dt * 32 + 8 * jg + 4 * hh2;
+                if constexpr (sizeof(T) == 2) {
+                  bf16x4 v;
 #pragma unroll
-              for (int e = 0; e < 4; ++e) v[e] = (bf16)(o[nt][dt][4 * jg + e] * inv);
-              *reinterpret_cast<bf16x4*>(op + d) = v;
-            } else {
-              f32x4 v;
+                  for (int e = 0; e < 4; ++e) v[e] = (bf16)(o[t][dt][4 * jg + e] * inv);
+                  *reinterpret_cast<bf16x4*>(op + d) = v;
+                } else {
+                  f32x4 v;
 #pragma unroll
-              for (int e = 0; e < 4; ++e) v[e] = o[nt][dt][4 * jg + e] * inv;
-              *reinterpret_cast<f32x4*>(op + d) = v;
-            }
+                  for (int e = 0; e < 4; ++e) v[e] = o[t][dt][4 * jg + e] * inv;
+                  *reinterpret_cast<f32x4*>(op + d) = v;
+                }
+              }
+          } else {
+            float* wp = A.ws_o + (slot * R + row) * D;
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+              for (int jg = 0; jg < 4; ++jg) {
+                const int d = dt * 32 + 8 * jg + 4 * hh2;
+                f32x4 v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = o[t][dt][4 * jg + e];
+                *reinterpret_cast<f32x4*>(wp + d) = v;
+              }
+            if (hh2 == 0) A.ws_ml[slot * R + row] = make_float2(mrun[t], ltot);
           }
-      } else {
-        float* wp = A.ws_o + (slot * R + row) * D;
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-          for (int jg = 0; jg < 4; ++jg) {
-            const int d = dt * 32 + 8 * jg + 4 * hh2;
-            f32x4 v;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = o[nt][dt][4 * jg + e];
-            *reinterpret_cast<f32x4*>(wp + d) = v;
-          }
-        if (hh2 == 0) A.ws_ml[slot * R + row] = make_float2(mrun[nt], ltot);
+        }
       }
     }
   }
@@ -422,17 +503,37 @@ __global__ __launch_bounds__(AT_THREADS) void attn_combine(Args<T, D> A) {
   const int64_t Ou = (int64_t)A.Hkv * sc.pb[bb] + (int64_t)g * N;
   const int wf = owner_of(Ou, Ttot, A.W), wl = owner_of(Ou + N - 1, Ttot, A.W);
   if (wf == wl) return;  // one workgroup held the whole unit and wrote the output itself
-  float M = -INFINITY;
-  for (int w = wf; w <= wl; ++w) M = fmaxf(M, A.ws_ml[((size_t)w + u) * R + row].x);
-  float L = 0.f;
+  // single pass over the unit's slots in workgroup order, CB slots' loads in flight at a time
+  constexpr int CB = 8;
+  float M = -INFINITY, L = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int w = wf; w <= wl; ++w) {
-    const size_t slot = (size_t)w + u;
-    const float2 ml = A.ws_ml[slot * R + row];
-    const float sc_w = tt_exp2((ml.x - M) * A.c);
-    L += ml.y * sc_w;
-    const f32x4 v = *reinterpret_cast<const f32x4*>(A.ws_o + (slot * R + row) * D + d);
-    acc += v * sc_w;
+  for (int w0 = wf; w0 <= wl; w0 += CB) {
+    float2 ml[CB];
+    f32x4 ov[CB];
+#pragma unroll
+    for (int k = 0; k < CB; ++k) {
+      const size_t slot = (size_t)(w0 + k) + u;
+      if (w0 + k <= wl) {
+        ml[k] = A.ws_ml[slot * R + row];
+        ov[k] = *reinterpret_cast<const f32x4*>(A.ws_o + (slot * R + row) * D + d);
+      } else {
+        ml[k] = make_float2(-INFINITY, 0.f);
+        ov[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    float bm = M;
+#pragma unroll
+    for (int k = 0; k < CB; ++k) bm = fmaxf(bm, ml[k].x);
+    const float rs = (M == -INFINITY) ? 0.f : tt_exp2((M - bm) * A.c);
+    L *= rs;
+    acc *= rs;
+#pragma unroll
+    for (int k = 0; k < CB; ++k) {
+      const float wk = (ml[k].x == -INFINITY) ? 0.f : tt_exp2((ml[k].x - bm) * A.c);
+      L += ml[k].y * wk;
+      acc += ov[k] * wk;
+    }
+    M = bm;
   }
   const float inv = 1.f / L;
   const int s = row / G, hq = g * G + row % G;
@@ -447,7 +548,10 @@ __global__ __launch_bounds__(AT_THREADS) void attn_combine(Args<T, D> A) {
   }
 }
 
-constexpr int MIN_KEYS_PER_WG = 128;
+#ifndef TT_AT_MIN_KEYS
+#define TT_AT_MIN_KEYS 128
+#endif
+constexpr int MIN_KEYS_PER_WG = TT_AT_MIN_KEYS;
 constexpr int AT_TARGET_WG = 256;
 
 template <typename T, int D>

@@ -43,3 +43,11 @@ __device__ __forceinline__ int tt_shfl_xor(int v, int mask) { return __shfl_xor(
 
 // exp2 on the hardware transcendental unit (v_exp_f32): exact at 0, returns 0 for -inf.
 __device__ __forceinline__ float tt_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Workgroup barrier for an LDS hand-off: waits for this wave's own LDS operations, then
+// s_barrier. Unlike __syncthreads() it does not wait for outstanding global loads, so prefetches
+// issued before it stay in flight. The "memory" clobber keeps the compiler from moving memory
+// accesses across it; register data of earlier global loads is still waited for where it is used.
+__device__ __forceinline__ void tt_lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}

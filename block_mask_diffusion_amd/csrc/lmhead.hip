@@ -5,73 +5,104 @@
 // H = 2688, V = 131072) W is 705 MB and is read exactly once; the product is HBM-bound unless M
 // reaches a few hundred rows.
 //
-// Workgroup = 4 waves = 256 vocabulary rows x (32*BMT) hidden rows. Each wave owns two 32-row
-// vocabulary tiles and every hidden row of the workgroup, so each W byte feeds exactly one wave:
-// W fragments go straight from HBM into a ring of registers RING steps (of 32 h each) ahead of
-// the MFMAs. The hidden rows are shared by the 4 waves and staged through LDS in double-buffered
-// chunks of KCH columns. MFMA tiles compute C[m][v] with W as the B operand, so the 32 lanes of a
-// result row hold 32 consecutive vocabulary ids and the fp32 stores are 128-byte coalesced.
+// Workgroup = 4 waves; each wave owns VT vocabulary tiles (NV rows each) and all MB = MT*BMT
+// hidden rows of the workgroup, so each W byte feeds exactly one wave: W fragments go straight
+// from HBM into a ring of registers RING pipeline steps (STEP values of h each) ahead of the
+// MFMAs. The hidden rows are shared by the 4 waves and staged through LDS in double-buffered
+// chunks of KCH columns. Tiles compute C[m][v] with W as the MFMA B operand, so result lanes
+// walk consecutive vocabulary ids and the fp32 stores are coalesced.
+//
+// Reduction order: inside a pipeline step the LPR lanes that share a W row split the STEP
+// columns into LPR contiguous spans, lane part p holding h = base + p*STEP/LPR + EPL*ks + i for
+// MFMA k-step ks. Each lane therefore reads one contiguous span of its W row per step (its 16-byte
+// loads walk consecutive addresses), and the hidden fragments read from LDS use the same order.
+//
 // When M needs several hidden-row blocks, the workgroups of one vocabulary tile are placed on the
-// same XCD (consecutive dispatch ids modulo 8 land on the same XCD), so the blocks share W in L2.
+// same XCD (dispatch ids congruent modulo 8 land on the same XCD), so the blocks share W in L2.
 #include "common.h"
 
 namespace {
 
 constexpr int LM_THREADS = 256;
 constexpr int LM_WAVES = 4;
-constexpr int VT_PER_WAVE = 2;
-constexpr int BV = LM_WAVES * VT_PER_WAVE * 32;  // vocabulary rows per workgroup
-constexpr int STEP = 32;                          // h per pipeline step
 constexpr int NXCD = 8;
 
-template <typename T>
-struct Lm;
+// MFMA shapes. Result layout (per lane l, register j):
+//   32x32: column l%32, row 8(j/4) + 4(l/32) + j%4 (16 registers)
+//   16x16: column l%16, row 4(l/16) + j            (4 registers)
+template <typename T, int MT>
+struct Shape;
 
 template <>
-struct Lm<bf16> {
-  static constexpr int KS = 16, EPL = 8, RING = 8;
-  static constexpr int KCH = 256;  // h per LDS chunk of hidden
+struct Shape<bf16, 32> {  // v_mfma_f32_32x32x16_bf16
+  static constexpr int NV = 32, LPR = 2, EPL = 8, NREG = 16;
   typedef bf16x8 frag;
-  __device__ static __forceinline__ f32x16 mma(frag a, frag b, f32x16 c) {
+  typedef f32x16 acc;
+  __device__ static __forceinline__ acc mma(frag a, frag b, acc c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
-  __device__ static __forceinline__ frag zero() {
-    frag f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) f[i] = (bf16)0.f;
-    return f;
-  }
+  __device__ static __forceinline__ int row(int lane, int j) { return 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3); }
 };
 
 template <>
-struct Lm<float> {
-  static constexpr int KS = 2, EPL = 1, RING = 2;
-  static constexpr int KCH = 64;
-  typedef float frag;
-  __device__ static __forceinline__ f32x16 mma(frag a, frag b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+struct Shape<bf16, 16> {  // v_mfma_f32_16x16x32_bf16
+  static constexpr int NV = 16, LPR = 4, NREG = 4;
+  [[maybe_unused]] static constexpr int EPL = 8;
+  typedef bf16x8 frag;
+  typedef f32x4 acc;
+  __device__ static __forceinline__ acc mma(frag a, frag b, acc c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
-  __device__ static __forceinline__ frag zero() { return 0.f; }
+  __device__ static __forceinline__ int row(int lane, int j) { return 4 * (lane >> 4) + j; }
 };
 
-template <typename T, int BMT>
-__global__ __launch_bounds__(LM_THREADS, 1) void lmhead_kernel(const T* __restrict__ hidden,
-                                                               const T* __restrict__ w,
-                                                               float* __restrict__ logits, int M,
-                                                               int H, int V, int nvt, int nmb) {
-  typedef Lm<T> L;
-  typedef typename L::frag frag;
-  constexpr int KS = L::KS, EPL = L::EPL, RING = L::RING, KCH = L::KCH;
-  constexpr int KPS = STEP / KS;            // MFMA k-steps per pipeline step
-  constexpr int MB = 32 * BMT;               // hidden rows per workgroup
+template <>
+struct Shape<float, 32> {  // v_mfma_f32_32x32x2f32
+  static constexpr int NV = 32, LPR = 2, EPL = 1, NREG = 16;
+  typedef float frag;
+  typedef f32x16 acc;
+  __device__ static __forceinline__ acc mma(frag a, frag b, acc c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ int row(int lane, int j) { return 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3); }
+};
+
+template <typename F>
+__device__ __forceinline__ F frag_zero() {
+  F f;
+  if constexpr (sizeof(F) == 4) {
+    f = 0.f;
+  } else {
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(F) / 2); ++i) f[i] = (bf16)0.f;
+  }
+  return f;
+}
+
+// T: element type; MT: MFMA rows (hidden rows per tile, 32 or 16); BMT: hidden tiles per
+// workgroup; VT: vocabulary tiles per wave; STEP: h per pipeline step; RING: steps in flight;
+// KCH: h per LDS chunk of hidden.
+template <typename T, int MT, int BMT, int VT, int STEP, int RING, int KCH>
+__global__ __launch_bounds__(LM_THREADS) void lmhead_kernel(const T* __restrict__ hidden,
+                                                           const T* __restrict__ w,
+                                                           float* __restrict__ logits, int M, int H,
+                                                           int V, int nvt, int nmb) {
+  typedef Shape<T, MT> SH;
+  typedef typename SH::frag frag;
+  typedef typename SH::acc acc_t;
+  constexpr int NV = SH::NV, LPR = SH::LPR, EPL = SH::EPL, NREG = SH::NREG;
+  constexpr int KI = LPR * EPL;          // reduction depth of one MFMA
+  constexpr int KPS = STEP / KI;         // MFMA k-steps per pipeline step
+  constexpr int SPAN = STEP / LPR;       // contiguous h per lane per step
+  constexpr int MB = MT * BMT;           // hidden rows per workgroup
+  constexpr int BV = LM_WAVES * VT * NV; // vocabulary rows per workgroup
   constexpr int HPAD = 16 / (int)sizeof(T);
   constexpr int HROW = KCH + HPAD;
   constexpr int EV = 16 / (int)sizeof(T);
-  constexpr int HVEC = MB * KCH / EV / LM_THREADS;  // 16-byte vectors per thread per chunk
+  constexpr int HVEC = (MB * KCH / EV + LM_THREADS - 1) / LM_THREADS;
+  static_assert(STEP % KI == 0 && KCH % STEP == 0, "tile shape");
   __shared__ __attribute__((aligned(16))) T hs[2][MB][HROW];
 
-  // XCD-aware tile order: dispatch id i runs on XCD i % 8; the nmb hidden-row blocks of one
-  // vocabulary tile get ids that differ by multiples of 8.
   const int id = blockIdx.x;
   int vtile, mblk;
   if (nmb == 1) {
@@ -87,32 +118,31 @@ __global__ __launch_bounds__(LM_THREADS, 1) void lmhead_kernel(const T* __restri
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int l32 = lane & 31, h2 = lane >> 5;
+  const int col = lane % NV, part = lane / NV;
   const int m0 = mblk * MB;
-  const int vbase = vtile * BV + wave * (VT_PER_WAVE * 32);
+  const int vbase = vtile * BV + wave * (VT * NV);
 
-  // W row pointers of this lane (one per vocabulary tile); rows past V read nothing
-  const T* wrow[VT_PER_WAVE];
-  bool wok[VT_PER_WAVE];
+  const T* wrow[VT];
+  bool wok[VT];
 #pragma unroll
-  for (int vt = 0; vt < VT_PER_WAVE; ++vt) {
-    const int v = vbase + vt * 32 + l32;
+  for (int vt = 0; vt < VT; ++vt) {
+    const int v = vbase + vt * NV + col;
     wok[vt] = v < V;
-    wrow[vt] = w + (size_t)(wok[vt] ? v : 0) * H;
+    wrow[vt] = w + (size_t)(wok[vt] ? v : 0) * H + part * SPAN;
   }
 
-  frag ring[RING][VT_PER_WAVE][KPS];
-  auto wload = [&](frag (&dst)[VT_PER_WAVE][KPS], int step) {
+  frag ring[RING][VT][KPS];
+  auto wload = [&](frag (&dst)[VT][KPS], int step) {
 #pragma unroll
-    for (int vt = 0; vt < VT_PER_WAVE; ++vt)
+    for (int vt = 0; vt < VT; ++vt)
 #pragma unroll
       for (int ks = 0; ks < KPS; ++ks) {
-        const int h = step * STEP + ks * KS + EPL * h2;
-        if (wok[vt]) {
-          if constexpr (EPL == 8) dst[vt][ks] = *reinterpret_cast<const frag*>(wrow[vt] + h);
-          else dst[vt][ks] = wrow[vt][h];
+        const T* p = wrow[vt] + step * STEP + ks * EPL;
+        if (wok[vt]) {  // several lanes/instructions share each W line: plain loads keep it in L2
+          if constexpr (EPL == 8) dst[vt][ks] = *reinterpret_cast<const frag*>(p);
+          else dst[vt][ks] = *p;
         } else {
-          dst[vt][ks] = L::zero();
+          dst[vt][ks] = frag_zero<frag>();
         }
       }
   };
@@ -125,8 +155,8 @@ __global__ __launch_bounds__(LM_THREADS, 1) void lmhead_kernel(const T* __restri
       const int v = tid + LM_THREADS * i;
       const int r = v / (KCH / EV), piece = v % (KCH / EV);
       const int m = m0 + r, h = hc0 + piece * EV;
-      hreg[i] = (m < M && h < H) ? *reinterpret_cast<const u32x4*>(hidden + (size_t)m * H + h)
-                                 : u32x4{0u, 0u, 0u, 0u};
+      hreg[i] = (r < MB && m < M && h < H) ? *reinterpret_cast<const u32x4*>(hidden + (size_t)m * H + h)
+                                          : u32x4{0u, 0u, 0u, 0u};
     }
   };
   auto hstore = [&](int buf) {
@@ -134,17 +164,17 @@ __global__ __launch_bounds__(LM_THREADS, 1) void lmhead_kernel(const T* __restri
     for (int i = 0; i < HVEC; ++i) {
       const int v = tid + LM_THREADS * i;
       const int r = v / (KCH / EV), piece = v % (KCH / EV);
-      *reinterpret_cast<u32x4*>(&hs[buf][r][piece * EV]) = hreg[i];
+      if (r < MB) *reinterpret_cast<u32x4*>(&hs[buf][r][piece * EV]) = hreg[i];
     }
   };
 
-  f32x16 acc[BMT][VT_PER_WAVE];
+  acc_t acc[BMT][VT];
 #pragma unroll
   for (int mt = 0; mt < BMT; ++mt)
 #pragma unroll
-    for (int vt = 0; vt < VT_PER_WAVE; ++vt)
+    for (int vt = 0; vt < VT; ++vt)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) acc[mt][vt][j] = 0.f;
+      for (int j = 0; j < NREG; ++j) acc[mt][vt][j] = 0.f;
 
   const int nsteps = H / STEP;
   const int nchunk = (H + KCH - 1) / KCH;
@@ -169,47 +199,243 @@ __global__ __launch_bounds__(LM_THREADS, 1) void lmhead_kernel(const T* __restri
 #pragma unroll
           for (int mt = 0; mt < BMT; ++mt) {
             frag a;
-            const int hcol = sc * STEP + ks * KS + EPL * h2;
-            if constexpr (EPL == 8) a = *reinterpret_cast<const frag*>(&hs[buf][mt * 32 + l32][hcol]);
-            else a = hs[buf][mt * 32 + l32][hcol];
+            const int hcol = sc * STEP + part * SPAN + ks * EPL;
+            if constexpr (EPL == 8) a = *reinterpret_cast<const frag*>(&hs[buf][mt * MT + col % MT][hcol]);
+            else a = hs[buf][mt * MT + col % MT][hcol];
 #pragma unroll
-            for (int vt = 0; vt < VT_PER_WAVE; ++vt) acc[mt][vt] = L::mma(a, ring[r][vt][ks], acc[mt][vt]);
+            for (int vt = 0; vt < VT; ++vt) acc[mt][vt] = SH::mma(a, ring[r][vt][ks], acc[mt][vt]);
           }
         }
         if (s + RING < nsteps) wload(ring[r], s + RING);
         if (sc == SPC - 1 || s == nsteps - 1) {  // chunk boundary: publish the next hidden chunk
           if (chunk + 1 < nchunk) hstore(buf ^ 1);
-          __syncthreads();
+          tt_lds_barrier();
         }
       }
     }
   }
 
-  // C[m][v]: lane l32 = vocabulary column, registers j = rows 8(j/4) + 4*h2 + j%4
 #pragma unroll
   for (int mt = 0; mt < BMT; ++mt)
 #pragma unroll
-    for (int vt = 0; vt < VT_PER_WAVE; ++vt) {
-      const int v = vbase + vt * 32 + l32;
+    for (int vt = 0; vt < VT; ++vt) {
+      const int v = vbase + vt * NV + col;
       if (v >= V) continue;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int m = m0 + mt * 32 + 8 * (j >> 2) + 4 * h2 + (j & 3);
+      for (int j = 0; j < NREG; ++j) {
+        const int m = m0 + mt * MT + SH::row(lane, j);
         if (m < M) logits[(size_t)m * V + v] = acc[mt][vt][j];
       }
     }
 }
 
-template <typename T, int BMT>
+template <typename T, int MT, int BMT, int VT, int STEP, int RING, int KCH>
 int lm_launch(const void* hidden, const void* w, float* logits, int M, int H, int V, hipStream_t s) {
+  constexpr int BV = LM_WAVES * VT * Shape<T, MT>::NV;
   const int nvt = (V + BV - 1) / BV;
-  const int nmb = (M + 32 * BMT - 1) / (32 * BMT);
+  const int nmb = (M + MT * BMT - 1) / (MT * BMT);
   unsigned grid;
   if (nmb == 1) grid = (unsigned)nvt;
   else grid = (unsigned)(((nvt + NXCD - 1) / NXCD) * NXCD * nmb);
-  hipLaunchKernelGGL((lmhead_kernel<T, BMT>), dim3(grid), dim3(LM_THREADS), 0, s, (const T*)hidden,
-                     (const T*)w, logits, M, H, V, nvt, nmb);
+  hipLaunchKernelGGL((lmhead_kernel<T, MT, BMT, VT, STEP, RING, KCH>), dim3(grid), dim3(LM_THREADS), 0, s,
+                     (const T*)hidden, (const T*)w, logits, M, H, V, nvt, nmb);
   return tt_launch_status();
+}
+
+
+// LDS-staged variant: W is read with whole-line coalesced 16-byte loads (consecutive lanes walk a
+// row; each 128-byte line is consumed by one instruction, so non-temporal loads are safe), staged
+// through LDS, and read back in MFMA operand layout. Workgroup = 4 waves x (VT tiles of NV rows);
+// each stage covers KW columns of h for the TV vocabulary rows and the MB hidden rows of the
+// workgroup. Two register sets keep two stages of global loads in flight.
+template <int MT, int BMT, int VT, int KW, bool NT, int NSET>
+__global__ __launch_bounds__(LM_THREADS) void lmhead_lds_kernel(const bf16* __restrict__ hidden,
+                                                               const bf16* __restrict__ w,
+                                                               float* __restrict__ logits, int M, int H,
+                                                               int V, int nvt, int nmb) {
+  typedef Shape<bf16, MT> SH;
+  typedef typename SH::frag frag;
+  typedef typename SH::acc acc_t;
+  constexpr int NV = SH::NV, LPR = SH::LPR, NREG = SH::NREG;
+  constexpr int KI = LPR * 8;             // reduction depth of one MFMA
+  constexpr int MB = MT * BMT;
+  constexpr int TV = LM_WAVES * VT * NV;   // vocabulary rows per workgroup
+  constexpr int ROW = KW + 8;              // LDS row (elements): 16-byte pad staggers banks
+  constexpr int VPR = KW / 8;              // 16-byte vectors per row per stage
+  constexpr int NWV = TV * VPR / LM_THREADS;
+  constexpr int NHV = (MB * VPR + LM_THREADS - 1) / LM_THREADS;
+  static_assert(TV * VPR % LM_THREADS == 0 && KW % KI == 0 && NSET % 2 == 0, "stage shape");
+  __shared__ __attribute__((aligned(16))) bf16 wsm[2][TV][ROW];
+  __shared__ __attribute__((aligned(16))) bf16 hsm[2][MB][ROW];
+
+  const int id = blockIdx.x;
+  int vtile, mblk;
+  if (nmb == 1) {
+    vtile = id;
+    mblk = 0;
+  } else {
+    const int grp = id / (NXCD * nmb);
+    const int rem = id - grp * NXCD * nmb;
+    mblk = rem / NXCD;
+    vtile = grp * NXCD + rem % NXCD;
+  }
+  if (vtile >= nvt) return;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int col = lane % NV, part = lane / NV;
+  const int m0 = mblk * MB, v0 = vtile * TV;
+
+  u32x4 wr[NSET][NWV], hr[NSET][NHV];
+  auto gload = [&](int set, int st) {
+    const int h0 = st * KW;
+#pragma unroll
+    for (int i = 0; i < NWV; ++i) {
+      const int v = tid + LM_THREADS * i;
+      const int r = v / VPR, pc = v % VPR;
+      const int vv = v0 + r;
+      const bf16* p = w + (size_t)vv * H + h0 + pc * 8;
+      if (vv < V) wr[set][i] = NT ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p))
+                                  : *reinterpret_cast<const u32x4*>(p);
+      else wr[set][i] = u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int i = 0; i < NHV; ++i) {
+      const int v = tid + LM_THREADS * i;
+      const int r = v / VPR, pc = v % VPR;
+      const int m = m0 + r;
+      hr[set][i] = (r < MB && m < M) ? *reinterpret_cast<const u32x4*>(hidden + (size_t)m * H + h0 + pc * 8)
+                                     : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto sstore = [&](int set, int buf) {
+#pragma unroll
+    for (int i = 0; i < NWV; ++i) {
+      const int v = tid + LM_THREADS * i;
+      *reinterpret_cast<u32x4*>(&wsm[buf][v / VPR][(v % VPR) * 8]) = wr[set][i];
+    }
+#pragma unroll
+    for (int i = 0; i < NHV; ++i) {
+      const int v = tid + LM_THREADS * i;
+      if (v / VPR < MB) *reinterpret_cast<u32x4*>(&hsm[buf][v / VPR][(v % VPR) * 8]) = hr[set][i];
+    }
+  };
+
+  acc_t acc[BMT][VT];
+#pragma unroll
+  for (int mt = 0; mt < BMT; ++mt)
+#pragma unroll
+    for (int vt = 0; vt < VT; ++vt)
+#pragma unroll
+      for (int j = 0; j < NREG; ++j) acc[mt][vt][j] = 0.f;
+
+  auto compute = [&](int buf) {
+#pragma unroll
+    for (int ks = 0; ks < KW / KI; ++ks) {
+      const int hc = ks * KI + part * 8;
+      frag b[VT];
+#pragma unroll
+      for (int vt = 0; vt < VT; ++vt)
+        b[vt] = *reinterpret_cast<const frag*>(&wsm[buf][(wave * VT + vt) * NV + col][hc]);
+#pragma unroll
+      for (int mt = 0; mt < BMT; ++mt) {
+        const frag a = *reinterpret_cast<const frag*>(&hsm[buf][mt * MT + col % MT][hc]);
+#pragma unroll
+        for (int vt = 0; vt < VT; ++vt) acc[mt][vt] = SH::mma(a, b[vt], acc[mt][vt]);
+      }
+    }
+  };
+
+  // stage g lives in register set g % NSET and LDS buffer g % 2; loads run NSET-1 stages ahead
+  const int nst = H / KW;
+#pragma unroll
+  for (int e = 0; e < NSET; ++e)
+    if (e < nst) gload(e, e);
+  sstore(0, 0);
+  __syncthreads();
+  for (int g0 = 0; g0 < nst; g0 += NSET) {
+#pragma unroll
+    for (int e = 0; e < NSET; ++e) {
+      const int g = g0 + e;
+      if (g < nst) {
+        compute(e & 1);
+        if (g + 1 < nst) sstore((e + 1) % NSET, (e + 1) & 1);
+        if (g + NSET < nst) gload(e, g + NSET);
+        tt_lds_barrier();
+      }
+    }
+  }
+
+#pragma unroll
+  for (int mt = 0; mt < BMT; ++mt)
+#pragma unroll
+    for (int vt = 0; vt < VT; ++vt) {
+      const int v = v0 + (wave * VT + vt) * NV + col;
+      if (v >= V) continue;
+#pragma unroll
+      for (int j = 0; j < NREG; ++j) {
+        const int m = m0 + mt * MT + SH::row(lane, j);
+        if (m < M) logits[(size_t)m * V + v] = acc[mt][vt][j];
+      }
+    }
+}
+
+template <int MT, int BMT, int VT, int KW, bool NT, int NSET>
+int lm_lds_launch(const void* hidden, const void* w, float* logits, int M, int H, int V, hipStream_t s) {
+  constexpr int TV = LM_WAVES * VT * Shape<bf16, MT>::NV;
+  const int nvt = (V + TV - 1) / TV;
+  const int nmb = (M + MT * BMT - 1) / (MT * BMT);
+  unsigned grid;
+  if (nmb == 1) grid = (unsigned)nvt;
+  else grid = (unsigned)(((nvt + NXCD - 1) / NXCD) * NXCD * nmb);
+  hipLaunchKernelGGL((lmhead_lds_kernel<MT, BMT, VT, KW, NT, NSET>), dim3(grid), dim3(LM_THREADS), 0, s,
+                     (const bf16*)hidden, (const bf16*)w, logits, M, H, V, nvt, nmb);
+  return tt_launch_status();
+}
+
+// Tile configurations (measured on MI355X at H = 2688, V = 131072):
+//   LDS-staged <MT, BMT, VT, KW, NT, NSET> per hidden-row bucket;
+//   direct <MT, BMT, VT, STEP, RING, KCH> for larger M, fp32, or H not a multiple of KW.
+#ifndef TT_LM_LDS16
+#define TT_LM_LDS16 16, 1, 2, 128, true, 4
+#endif
+#ifndef TT_LM_LDS64
+#define TT_LM_LDS64 16, 4, 1, 128, true, 4
+#endif
+#ifndef TT_LM_LDS128
+#define TT_LM_LDS128 32, 4, 1, 64, true, 4
+#endif
+#ifndef TT_LM_CFG32
+#define TT_LM_CFG32 32, 1, 2, 32, 8, 256
+#endif
+#ifndef TT_LM_CFG64
+#define TT_LM_CFG64 32, 2, 2, 32, 8, 256
+#endif
+#ifndef TT_LM_CFGBIG
+#define TT_LM_CFGBIG 32, 4, 2, 32, 8, 256
+#endif
+
+// Runs the LDS-staged kernel when the stage width divides H; returns 1 when it does not apply.
+template <int MT, int BMT, int VT, int KW, bool NT, int NSET>
+int lm_try_lds(const void* h, const void* w, float* o, int M, int H, int V, hipStream_t s) {
+  if (H % KW != 0) return 1;
+  return lm_lds_launch<MT, BMT, VT, KW, NT, NSET>(h, w, o, M, H, V, s);
+}
+
+template <int MT, int BMT, int VT, int STEP, int RING, int KCH>
+int lm_direct(const void* h, const void* w, float* o, int M, int H, int V, hipStream_t s) {
+  if (H % STEP != 0) return lm_launch<bf16, MT, BMT, VT, 32, RING * STEP / 32, KCH>(h, w, o, M, H, V, s);
+  return lm_launch<bf16, MT, BMT, VT, STEP, RING, KCH>(h, w, o, M, H, V, s);
+}
+
+int lm_bf16(const void* h, const void* w, float* o, int M, int H, int V, hipStream_t s) {
+  int st = 1;
+  if (M <= 16) st = lm_try_lds<TT_LM_LDS16>(h, w, o, M, H, V, s);
+  else if (M <= 64) st = lm_try_lds<TT_LM_LDS64>(h, w, o, M, H, V, s);
+  else if (M <= 128) st = lm_try_lds<TT_LM_LDS128>(h, w, o, M, H, V, s);
+  if (st != 1) return st;
+  if (M <= 32) return lm_direct<TT_LM_CFG32>(h, w, o, M, H, V, s);
+  if (M <= 64) return lm_direct<TT_LM_CFG64>(h, w, o, M, H, V, s);
+  return lm_direct<TT_LM_CFGBIG>(h, w, o, M, H, V, s);
 }
 
 }  // namespace
@@ -222,11 +448,7 @@ extern "C" int tt_lmhead_logits(const void* hidden, const void* w, float* logits
   if (H % 32 != 0) return TT_ERR_UNSUPPORTED;
   if ((uintptr_t)hidden % 16 || (uintptr_t)w % 16) return TT_ERR_ARG;
   hipStream_t s = (hipStream_t)stream;
-  if (dtype == TT_BF16) {
-    if (M <= 32) return lm_launch<bf16, 1>(hidden, w, logits, M, H, V, s);
-    if (M <= 64) return lm_launch<bf16, 2>(hidden, w, logits, M, H, V, s);
-    return lm_launch<bf16, 4>(hidden, w, logits, M, H, V, s);
-  }
-  if (M <= 32) return lm_launch<float, 1>(hidden, w, logits, M, H, V, s);
-  return lm_launch<float, 4>(hidden, w, logits, M, H, V, s);
+  if (dtype == TT_BF16) return lm_bf16(hidden, w, logits, M, H, V, s);
+  if (M <= 32) return lm_launch<float, 32, 1, 2, 32, 2, 64>(hidden, w, logits, M, H, V, s);
+  return lm_launch<float, 32, 4, 2, 32, 2, 64>(hidden, w, logits, M, H, V, s);
 }

@@ -6,9 +6,10 @@
 //                   sum of exp(l - max)), the mask id's logit counting as -inf. HBM-bound: each
 //                   logit of a masked row is read exactly once; rows already committed are skipped
 //                   without reading anything but their mask word.
-//   unmask_commit   one wave per block: lane i merges row i's chunk partials in a fixed order
-//                   (deterministic), gets conf = 1 / sum and the prediction, then applies the
-//                   threshold, the completion floor and the in-place token / bitmap update.
+//   unmask_commit   one workgroup per block: row i's chunk partials are merged in a fixed order
+//                   (deterministic) by four waves in parallel; lane i of wave 0 then holds
+//                   conf = 1 / sum and the prediction and applies the threshold, the completion
+//                   floor and the in-place token / bitmap update.
 #include "common.h"
 
 namespace {
@@ -123,28 +124,54 @@ __global__ __launch_bounds__(UM_THREADS) void unmask_partial(const float* __rest
   }
 }
 
-__global__ __launch_bounds__(TT_WAVE) void unmask_commit(const Partial* __restrict__ ws,
-                                                         int32_t* __restrict__ tokens,
-                                                         uint64_t* __restrict__ mask_bits,
-                                                         int32_t* __restrict__ n_masked,
-                                                         float* __restrict__ conf_out,
-                                                         int32_t* __restrict__ pred_out, int S,
-                                                         int nchunk, int step, int num_steps,
-                                                         float gamma) {
+constexpr int CM_THREADS = 256;
+constexpr int CM_Q = CM_THREADS / TT_WAVE;  // chunk stripes merged in parallel per row
+constexpr int CM_BATCH = 8;                 // partial loads issued before merging
+
+// One workgroup per block. Thread (stripe q, row i) merges the partials c = q, q+4, q+8, ... of
+// row i, issuing a batch of loads before merging them in increasing c; wave 0 then merges the four
+// stripes in the order q = 0..3 (a fixed order: bitwise reproducible), so lane i holds row i's
+// confidence and prediction, and applies the commit rule for the block.
+__global__ __launch_bounds__(CM_THREADS) void unmask_commit(const Partial* __restrict__ ws,
+                                                           int32_t* __restrict__ tokens,
+                                                           uint64_t* __restrict__ mask_bits,
+                                                           int32_t* __restrict__ n_masked,
+                                                           float* __restrict__ conf_out,
+                                                           int32_t* __restrict__ pred_out, int S,
+                                                           int nchunk, int step, int num_steps,
+                                                           float gamma) {
+  __shared__ float pm[CM_Q][TT_WAVE], ps[CM_Q][TT_WAVE];
+  __shared__ int pa[CM_Q][TT_WAVE];
   const int b = blockIdx.x;
-  const int i = threadIdx.x;
+  const int i = threadIdx.x & (TT_WAVE - 1), q = threadIdx.x / TT_WAVE;
   const uint64_t bits = mask_bits[b];
   const bool masked = (i < S) && ((bits >> i) & 1ull);
+  float m = -INFINITY, s = 0.f;
+  int a = INT32_MAX;
+  if (masked) {
+    const Partial* p = ws + (size_t)(b * S + i) * nchunk;
+    for (int c0 = q; c0 < nchunk; c0 += CM_Q * CM_BATCH) {
+      Partial x[CM_BATCH];
+#pragma unroll
+      for (int k = 0; k < CM_BATCH; ++k) {
+        const int c = c0 + CM_Q * k;
+        if (c < nchunk) x[k] = p[c];
+        else x[k] = Partial{-INFINITY, 0.f, INT32_MAX, 0};
+      }
+#pragma unroll
+      for (int k = 0; k < CM_BATCH; ++k) merge(m, a, s, x[k].m, x[k].a, x[k].s);
+    }
+  }
+  pm[q][i] = m;
+  ps[q][i] = s;
+  pa[q][i] = a;
+  __syncthreads();
+  if (q != 0) return;
+#pragma unroll
+  for (int k = 1; k < CM_Q; ++k) merge(m, a, s, pm[k][i], pa[k][i], ps[k][i]);
   float conf = -1.f;
   int pred = -1;
   if (masked) {
-    const Partial* p = ws + (size_t)(b * S + i) * nchunk;
-    float m = -INFINITY, s = 0.f;
-    int a = INT32_MAX;
-    for (int c = 0; c < nchunk; ++c) {  // fixed order: bitwise reproducible
-      Partial q = p[c];
-      merge(m, a, s, q.m, q.a, q.s);
-    }
     conf = 1.f / s;
     pred = a;
   }
@@ -207,7 +234,7 @@ extern "C" int tt_confidence_unmask(const float* logits, int32_t* tokens, uint64
     hipLaunchKernelGGL(unmask_partial<false>, grid, dim3(UM_THREADS), 0, s, logits, mask_bits, ws,
                        S, V, nchunk, mask_id);
   if (tt_launch_status() != TT_OK) return TT_ERR_HIP;
-  hipLaunchKernelGGL(unmask_commit, dim3(B), dim3(TT_WAVE), 0, s, ws, tokens, mask_bits, n_masked,
+  hipLaunchKernelGGL(unmask_commit, dim3(B), dim3(CM_THREADS), 0, s, ws, tokens, mask_bits, n_masked,
                      conf_out, pred_out, S, nchunk, step, num_steps, gamma);
   return tt_launch_status();
 }
