@@ -30,7 +30,6 @@ sys.path.insert(0, ROOT)
 METRIC = "denoise block-steps/s + committed tokens/s; % HBM roofline (attn), % MFMA (LM head)"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 MFMA
-PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "lmhead_w1_traffic.txt")
 
 
 def parse():
@@ -60,27 +59,38 @@ def algorithmic(wl):
     return dict(attn_bytes=attn_bytes, attn_flops=attn_flops, lm_bytes=lm_bytes, lm_flops=lm_flops)
 
 
-def read_traffic(src_hash):
-    """HBM bytes per launch of the LM-head kernel from the committed counter summary, if it was
-    taken on the current kernel source; else None."""
+TRAFFIC_SOURCES = {"lmhead": ("lmhead.hip", "common.h"), "attn": ("attn.hip", "common.h")}
+
+
+def read_traffic(kind, wid):
+    """HBM bytes per call of `kind` ("lmhead" or "attn") from the committed counter summary
+    profiles/<kind>_w<wid>_traffic.txt, if it was taken at this workload and on the current
+    kernel code; else None."""
     try:
         kv = {}
-        for line in open(PROFILE_TRAFFIC):
+        for line in open(os.path.join(ROOT, "profiles", f"{kind}_w{wid}_traffic.txt")):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
-        if kv.get("source_sha256") != src_hash:
+        if kv.get("source_sha256") != source_hash(kind) or kv.get("workload") != f"w{wid}":
             return None
         return float(kv["hbm_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
         return None
 
 
-def source_hash():
+def source_hash(kind):
+    """sha256 of a kernel's code (its .hip file + common.h) with // comments, trailing blanks and
+    blank lines removed, so that editing a comment does not void a traffic record."""
     import hashlib
+    import re
     h = hashlib.sha256()
-    for f in ("lmhead.hip", "common.h"):
-        h.update(open(os.path.join(ROOT, "block_mask_diffusion_amd", "csrc", f), "rb").read())
+    for f in TRAFFIC_SOURCES[kind]:
+        text = open(os.path.join(ROOT, "block_mask_diffusion_amd", "csrc", f)).read()
+        for line in text.splitlines():
+            line = re.sub(r"//.*$", "", line).rstrip()
+            if line:
+                h.update(line.encode() + b"\n")
     return h.hexdigest()
 
 
@@ -250,14 +260,14 @@ def main():
     times = {"attn": t_attn, "lmhead": t_lm, "unmask": t_um}
     dominant = max(times, key=times.get)
     if dominant == "lmhead":
-        traffic = read_traffic(source_hash())
+        traffic = read_traffic("lmhead", wl.wid)
         roof = {"kernel": "lmhead_lds_kernel (tt_lmhead_logits)", "bound": "hbm", "achieved": round(lm_gbs, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(lm_gbs / HBM_PEAK_GBS, 4),
                 "traffic": traffic, "algorithmic_bytes": alg["lm_bytes"], "avg_launch_us": round(t_lm * 1e3, 2)}
     elif dominant == "attn":
         roof = {"kernel": "attn_partial + attn_combine (tt_block_attn)", "bound": "hbm",
                 "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": read_traffic("attn", wl.wid),
                 "algorithmic_bytes": alg["attn_bytes"], "avg_launch_us": round(t_attn_call * 1e3, 2)}
     else:
         roof = {"kernel": "unmask (tt_confidence_unmask)", "bound": "hbm", "achieved": round(um_gbs, 1),

@@ -11,7 +11,7 @@
 // in slot w + u of the workspace, which attn_combine merges in a fixed order. Slot w + u is
 // injective because walking the pieces in order raises w or u (or both) at every boundary.
 //
-// Inside a workgroup (4 waves, two 32-row query tiles each): K/V stages of KC keys go straight from
+// Inside a workgroup (8 waves, one 32-row query tile each): K/V stages of KC keys go straight from
 // HBM into an LDS ring of NBUF stages (direct global->LDS loads, three stages in flight) and are
 // shared by all S*G query rows (up to 256), so every key byte is read from HBM once. Scores are
 // computed transposed, S^T = K Q^T, on 32x32 MFMA tiles: the result layout gives each lane one

@@ -247,7 +247,8 @@ int lm_launch(const void* hidden, const void* w, float* logits, int M, int H, in
 // row; each 128-byte line is consumed by one instruction, so non-temporal loads are safe), staged
 // through LDS, and read back in MFMA operand layout. Workgroup = 4 waves x (VT tiles of NV rows);
 // each stage covers KW columns of h for the TV vocabulary rows and the MB hidden rows of the
-// workgroup. Two register sets keep two stages of global loads in flight.
+// workgroup. NSET register sets keep up to NSET stages of global loads in flight; LDS is double
+// buffered, so one barrier per stage separates the writes of stage g+1 from the reads of stage g.
 template <int MT, int BMT, int VT, int KW, bool NT, int NSET>
 __global__ __launch_bounds__(LM_THREADS) void lmhead_lds_kernel(const bf16* __restrict__ hidden,
                                                                const bf16* __restrict__ w,
