@@ -7,9 +7,10 @@
 // Work split (flash-decoding with stream-K balance): the key lists of all units, laid end to end,
 // form one key space of T keys; workgroup w takes keys [floor(w*T/W), floor((w+1)*T/W)). A range
 // can span several units; each (workgroup, unit) piece either covers the whole unit (the output is
-// normalised and written directly) or leaves an fp32 partial (unnormalised O, running max, sum)
-// in slot w + u of the workspace, which attn_combine merges in a fixed order. Slot w + u is
-// injective because walking the pieces in order raises w or u (or both) at every boundary.
+// normalised and written directly) or leaves an fp32 partial (O / l, with the running max m and
+// the sum l) in slot w + u of the workspace, which attn_combine merges in
+// a fixed order. Slot w + u is injective because walking the pieces in order raises w or u (or
+// both) at every boundary.
 //
 // Inside a workgroup (8 waves, one 32-row query tile each): K/V stages of KC keys go straight from
 // HBM into an LDS ring of NBUF stages (direct global->LDS loads, three stages in flight) and are
@@ -59,6 +60,19 @@ struct Mf<bf16> {
     for (int i = 0; i < 8; ++i) f[i] = (bf16)p[8 * u + i];
     return f;
   }
+  // acc + sum of the 16 bf16 probabilities of this lane, by pairs (v_dot2 with (1, 1))
+  __device__ static __forceinline__ float psum(const frag (&pf)[2], const f32x16&, float acc) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 one = {(bf16)1.f, (bf16)1.f};
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[u], pf[u], 0, 1), one, acc, false);
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[u], pf[u], 2, 3), one, acc, false);
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[u], pf[u], 4, 5), one, acc, false);
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[u], pf[u], 6, 7), one, acc, false);
+    }
+    return acc;
+  }
 };
 
 template <>
@@ -71,6 +85,13 @@ struct Mf<float> {
   }
   // register u of lane half h holds key 8(u/4) + 4h + u%4 and feeds reduction slot 2u + h
   __device__ static __forceinline__ frag pfrag(const f32x16& p, int u) { return p[u]; }
+  template <int N>
+  __device__ static __forceinline__ float psum(const frag (&)[N], const f32x16& p, float acc) {
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) s += p[j];
+    return acc + s;
+  }
 };
 
 // Stage geometry: KC keys per stage (64 for bf16, 32 for fp32), K and V stored row-major in an
@@ -148,6 +169,12 @@ __device__ __forceinline__ int owner_of(int64_t x, int64_t T, int W) {
   return (int)(((x + 1) * W - 1) / T);
 }
 
+// Element type of the split-K partial outputs (normalised O / l): fp32 for every input type. A
+// bf16 partial would add a second rounding of up to 2^-8 |o| on top of the output's own bf16
+// rounding, which for outputs near single value rows (|o| of a few units) breaks a 1e-2 bound.
+template <typename T>
+using PartT = float;
+
 template <typename T, int D>
 struct Args {
   const T* q;
@@ -158,8 +185,8 @@ struct Args {
   const int32_t* ctx_start;
   const int32_t* ctx_len;
   T* out;
-  float* ws_o;   // [slots][R][D]
-  float2* ws_ml; // [slots][R] (running max of raw scores, sum)
+  PartT<T>* ws_o;  // [slots][R][D]: normalised partial output O / l
+  float2* ws_ml;   // [slots][R]: (running max of the raw scores m, sum l relative to m)
   int B, S, Hq, Hkv;
   int64_t ctx_rows;
   int W;
@@ -172,6 +199,33 @@ __device__ __forceinline__ void wait_vmem() {  // this wave's oldest outstanding
 }
 
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+// LDS byte address of a __shared__ location, made wave-uniform (it goes to M0).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)LDS_PTR(const void, p));
+}
+
+// Direct global->LDS load of 16 bytes per lane: lane i's bytes land at LDS address base + 16 i.
+// Written as inline asm on purpose: the compiler then does not track these writes to LDS, so it
+// does not put a wait for every outstanding global load in front of each LDS read of the ring.
+// Ordering is explicit instead: each stage's readers wait (counted vmcnt, then a barrier) for
+// that stage's loads only, and a buffer is refilled only after the barrier that ends its reads.
+// M0 (which holds the LDS base) is saved to a scratch SGPR and restored inside the same asm, so
+// the compiler's own use of M0 is unaffected. The only register output is that scratch SGPR,
+// written by a scalar move; the load itself returns nothing to registers.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"  // one wait state between an SALU write of M0 and its use by an LDS DMA
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_nop 0\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(gptr), "s"(lds_base)
+      : "memory");
+}
 
 template <typename T, int D>
 __global__ __launch_bounds__(AT_THREADS, 1) void attn_partial(Args<T, D> A) {
@@ -278,10 +332,8 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_partial(Args<T, D> A) {
         const int gk = slot ^ GE::fk(r), gv = slot ^ GE::fv(r);
         const T* kp = key < P ? kctx + (size_t)key * D : kblk + (size_t)(key - P) * blk_stride;
         const T* vp = key < P ? vctx + (size_t)key * D : vblk + (size_t)(key - P) * blk_stride;
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<const unsigned char*>(kp) + 16 * gk,
-                                         LDS_PTR(void, &ring.k[buf][chunk * 1024]), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<const unsigned char*>(vp) + 16 * gv,
-                                         LDS_PTR(void, &ring.v[buf][chunk * 1024]), 16, 0, 0);
+        dma16(reinterpret_cast<const unsigned char*>(kp) + 16 * gk, lds_addr(&ring.k[buf][chunk * 1024]));
+        dma16(reinterpret_cast<const unsigned char*>(vp) + 16 * gv, lds_addr(&ring.v[buf][chunk * 1024]));
       }
     };
     // stage st resident: wait for this wave's loads of stage st (the later stages stay in flight),
@@ -314,23 +366,12 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_partial(Args<T, D> A) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) acc[t][j] = 0.f;
       if (TT_AT_PRIO) __builtin_amdgcn_s_setprio(2);  // MFMA phase: let this wave issue first
-      if constexpr (TPW == 1) {
-        // two accumulation chains (even / odd k-steps) so consecutive MFMAs are independent
-        f32x16 acc2;
+      // one accumulation chain per tile: back-to-back MFMAs into the same accumulator need no
+      // extra wait states, and a second chain would cost 16 adds to merge
 #pragma unroll
-        for (int j = 0; j < 16; ++j) acc2[j] = 0.f;
+      for (int ks = 0; ks < D / KS; ++ks)
 #pragma unroll
-        for (int ks = 0; ks < D / KS; ks += 2) {
-          acc[0] = MF::mma(kf[ks], qf[0][ks], acc[0]);
-          acc2 = MF::mma(kf[ks + 1], qf[0][ks + 1], acc2);
-        }
-        acc[0] += acc2;
-      } else {
-#pragma unroll
-        for (int ks = 0; ks < D / KS; ++ks)
-#pragma unroll
-          for (int t = 0; t < TPW; ++t) acc[t] = MF::mma(kf[ks], qf[t][ks], acc[t]);
-      }
+        for (int t = 0; t < TPW; ++t) acc[t] = MF::mma(kf[ks], qf[t][ks], acc[t]);
       if (TT_AT_PRIO) __builtin_amdgcn_s_setprio(0);
     };
     // V^T fragment of MFMA uu / d-tile dt: keys of the P registers 8uu..8uu+7 of this lane half
@@ -381,6 +422,13 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_partial(Args<T, D> A) {
             kread(kbuf, kt, kf);
             f32x16 sacc[TPW];
             qk(kf, sacc);
+            // V^T fragments of the whole sub-tile, issued now so that their LDS latency is
+            // hidden behind the softmax below (they do not depend on it)
+            frag va[D / 32][32 / KS];
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+              for (int uu = 0; uu < 32 / KS; ++uu) va[dt][uu] = vfrag(vbuf, kt, uu, dt);
             frag pf[TPW][32 / KS];
 #pragma unroll
             for (int t = 0; t < TPW; ++t) {
@@ -393,7 +441,7 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_partial(Args<T, D> A) {
 #pragma unroll
               for (int j = 3; j < 15; j += 2) mx = fmaxf(fmaxf(mx, sacc[t][j]), sacc[t][j + 1]);
               mx = fmaxf(mx, sacc[t][15]);
-              mx = fmaxf(mx, tt_shfl_xor(mx, 32));
+              mx = fmaxf(mx, tt_swap_halves(mx));
               // Lazy rescale: the reference max only moves when a row's max grows by more than
               // 2^8 in the exponent; exponentials stay <= 256 and the final normalisation is exact.
               if (__ballot((mx - mrun[t]) * A.c > RESCALE_LOG2)) {
@@ -407,35 +455,27 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_partial(Args<T, D> A) {
                 mrun[t] = mnew;
               }
               const float mc = mrun[t] * A.c;
-              float ls = 0.f;
 #pragma unroll
-              for (int j = 0; j < 16; ++j) {
-                const float p = tt_exp2(fmaf(sacc[t][j], A.c, -mc));
-                sacc[t][j] = p;
-                ls += p;
-              }
-              lrun[t] += ls;
+              for (int j = 0; j < 16; ++j) sacc[t][j] = tt_exp2(fmaf(sacc[t][j], A.c, -mc));
 #pragma unroll
               for (int uu = 0; uu < 32 / KS; ++uu) pf[t][uu] = MF::pfrag(sacc[t], uu);
+              // row sum of the probabilities exactly as the PV product uses them
+              lrun[t] = MF::psum(pf[t], sacc[t], lrun[t]);
             }
             if (TT_AT_PRIO) __builtin_amdgcn_s_setprio(2);
 #pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt) {
-              frag va[32 / KS];
-#pragma unroll
-              for (int uu = 0; uu < 32 / KS; ++uu) va[uu] = vfrag(vbuf, kt, uu, dt);
+            for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
               for (int uu = 0; uu < 32 / KS; ++uu)
 #pragma unroll
-                for (int t = 0; t < TPW; ++t) o[t][dt] = MF::mma(va[uu], pf[t][uu], o[t][dt]);
-            }
+                for (int t = 0; t < TPW; ++t) o[t][dt] = MF::mma(va[dt][uu], pf[t][uu], o[t][dt]);
             if (TT_AT_PRIO) __builtin_amdgcn_s_setprio(0);
           }
         }
       }
     }
 
-    // ---- epilogue: direct normalised output, or an fp32 partial in slot w + u
+    // ---- epilogue: direct normalised output, or a normalised partial in slot w + u
     if (active) {
       const size_t slot = (size_t)w + u;
 #pragma unroll
@@ -465,16 +505,19 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_partial(Args<T, D> A) {
                 }
               }
           } else {
-            float* wp = A.ws_o + (slot * R + row) * D;
+            typedef PartT<T> PT;
+            typedef PT pvec __attribute__((ext_vector_type(4)));
+            PT* wp = A.ws_o + (slot * R + row) * D;
+            const float inv = 1.f / ltot;
 #pragma unroll
             for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
               for (int jg = 0; jg < 4; ++jg) {
                 const int d = dt * 32 + 8 * jg + 4 * hh2;
-                f32x4 v;
+                pvec v;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = o[t][dt][4 * jg + e];
-                *reinterpret_cast<f32x4*>(wp + d) = v;
+                for (int e = 0; e < 4; ++e) v[e] = (PT)(o[t][dt][4 * jg + e] * inv);
+                *reinterpret_cast<pvec*>(wp + d) = v;
               }
             if (hh2 == 0) A.ws_ml[slot * R + row] = make_float2(mrun[t], ltot);
           }
@@ -484,41 +527,77 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_partial(Args<T, D> A) {
   }
 }
 
-// Merge the partials of units split across workgroups, in workgroup order (deterministic).
+constexpr int CB_THREADS = 128;
+
+// Block-wide sum of two 64-bit values (CB_THREADS threads).
+__device__ __forceinline__ void block_sum2(int64_t& a, int64_t& b) {
+  __shared__ int64_t red[2][CB_THREADS / TT_WAVE];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    a += __shfl_xor(a, off, TT_WAVE);
+    b += __shfl_xor(b, off, TT_WAVE);
+  }
+  const int wv = threadIdx.x / TT_WAVE;
+  if ((threadIdx.x & (TT_WAVE - 1)) == 0) {
+    red[0][wv] = a;
+    red[1][wv] = b;
+  }
+  __syncthreads();
+  a = 0;
+  b = 0;
+#pragma unroll
+  for (int k = 0; k < CB_THREADS / TT_WAVE; ++k) {
+    a += red[0][k];
+    b += red[1][k];
+  }
+}
+
+// Split-K merge of one unit's normalised partials, in workgroup order (fixed, so the result is
+// reproducible): O = sum_k e^(m_k - M) l_k Ohat_k / sum_k e^(m_k - M) l_k. Each thread owns VPT
+// consecutive output elements of one query row (one 16-byte load per partial).
 template <typename T, int D>
-__global__ __launch_bounds__(AT_THREADS) void attn_combine(Args<T, D> A) {
-  __shared__ Scan sc;
-  constexpr int TPR = D / 4;              // threads per query row (4 values each)
-  constexpr int RPB = AT_THREADS / TPR;   // rows per workgroup
+__global__ __launch_bounds__(CB_THREADS) void attn_combine(Args<T, D> A) {
+  typedef PartT<T> PT;
+  constexpr int VPT = 16 / (int)sizeof(PT);  // elements per thread
+  constexpr int TPR = D / VPT;               // threads per query row
+  constexpr int RPB = CB_THREADS / TPR;      // rows per workgroup
   const int G = A.Hq / A.Hkv;
   const int R = A.S * G;
   const int u = blockIdx.y;
   const int bb = u / A.Hkv, g = u - bb * A.Hkv;
-  scan_lengths(sc, A.ctx_len, A.B, A.S);
+  // key-space offsets: sum of N_b' = ctx_len[b'] + S over b' < bb, and over all b'
+  int64_t before = 0, total = 0;
+  for (int b2 = threadIdx.x; b2 < A.B; b2 += CB_THREADS) {
+    const int64_t n = (int64_t)A.ctx_len[b2] + A.S;
+    total += n;
+    if (b2 < bb) before += n;
+  }
+  block_sum2(before, total);
   const int row = blockIdx.x * RPB + threadIdx.x / TPR;
-  const int d = (threadIdx.x % TPR) * 4;
+  const int d = (threadIdx.x % TPR) * VPT;
   if (row >= R) return;
-  const int64_t Ttot = (int64_t)A.Hkv * sc.pb[A.B];
-  const int N = sc.pb[bb + 1] - sc.pb[bb];
-  const int64_t Ou = (int64_t)A.Hkv * sc.pb[bb] + (int64_t)g * N;
+  const int64_t Ttot = (int64_t)A.Hkv * total;
+  const int N = A.ctx_len[bb] + A.S;
+  const int64_t Ou = (int64_t)A.Hkv * before + (int64_t)g * N;
   const int wf = owner_of(Ou, Ttot, A.W), wl = owner_of(Ou + N - 1, Ttot, A.W);
   if (wf == wl) return;  // one workgroup held the whole unit and wrote the output itself
-  // single pass over the unit's slots in workgroup order, CB slots' loads in flight at a time
-  constexpr int CB = 8;
+  constexpr int CB = 8;  // partials whose loads are in flight together
   float M = -INFINITY, L = 0.f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float acc[VPT];
+#pragma unroll
+  for (int e = 0; e < VPT; ++e) acc[e] = 0.f;
   for (int w0 = wf; w0 <= wl; w0 += CB) {
     float2 ml[CB];
-    f32x4 ov[CB];
+    u32x4 ov[CB];
 #pragma unroll
     for (int k = 0; k < CB; ++k) {
       const size_t slot = (size_t)(w0 + k) + u;
       if (w0 + k <= wl) {
         ml[k] = A.ws_ml[slot * R + row];
-        ov[k] = *reinterpret_cast<const f32x4*>(A.ws_o + (slot * R + row) * D + d);
+        ov[k] = *reinterpret_cast<const u32x4*>(A.ws_o + (slot * R + row) * D + d);
       } else {
         ml[k] = make_float2(-INFINITY, 0.f);
-        ov[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+        ov[k] = u32x4{0u, 0u, 0u, 0u};
       }
     }
     float bm = M;
@@ -526,26 +605,26 @@ __global__ __launch_bounds__(AT_THREADS) void attn_combine(Args<T, D> A) {
     for (int k = 0; k < CB; ++k) bm = fmaxf(bm, ml[k].x);
     const float rs = (M == -INFINITY) ? 0.f : tt_exp2((M - bm) * A.c);
     L *= rs;
-    acc *= rs;
+#pragma unroll
+    for (int e = 0; e < VPT; ++e) acc[e] *= rs;
 #pragma unroll
     for (int k = 0; k < CB; ++k) {
-      const float wk = (ml[k].x == -INFINITY) ? 0.f : tt_exp2((ml[k].x - bm) * A.c);
-      L += ml[k].y * wk;
-      acc += ov[k] * wk;
+      const float wk = (ml[k].x == -INFINITY) ? 0.f : tt_exp2((ml[k].x - bm) * A.c) * ml[k].y;
+      L += wk;
+      const PT* pv = reinterpret_cast<const PT*>(&ov[k]);
+#pragma unroll
+      for (int e = 0; e < VPT; ++e) acc[e] = fmaf((float)pv[e], wk, acc[e]);
     }
     M = bm;
   }
   const float inv = 1.f / L;
   const int s = row / G, hq = g * G + row % G;
   T* op = A.out + (((size_t)bb * A.S + s) * A.Hq + hq) * D + d;
-  if constexpr (sizeof(T) == 2) {
-    bf16x4 v;
+  typedef T ovec __attribute__((ext_vector_type(VPT)));  // exactly this thread's VPT outputs
+  ovec v;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = (bf16)(acc[e] * inv);
-    *reinterpret_cast<bf16x4*>(op) = v;
-  } else {
-    *reinterpret_cast<f32x4*>(op) = acc * inv;
-  }
+  for (int e = 0; e < VPT; ++e) v[e] = (T)(acc[e] * inv);
+  *reinterpret_cast<ovec*>(op) = v;
 }
 
 #ifndef TT_AT_MIN_KEYS
@@ -566,7 +645,7 @@ int launch(const void* q, const void* kb, const void* vb, const void* kc, const 
   int W = (int)std::min<int64_t>((int64_t)AT_TARGET_WG, (tmax + MIN_KEYS_PER_WG - 1) / MIN_KEYS_PER_WG);
   if (W < 1) W = 1;
   const size_t slots = (size_t)W + U;
-  const size_t o_bytes = tt_align_up(slots * R * D * sizeof(float), 256);
+  const size_t o_bytes = tt_align_up(slots * R * D * sizeof(PartT<T>), 256);
   const size_t need = o_bytes + tt_align_up(slots * R * sizeof(float2), 256);
   int st = tt_workspace_check(ws, ws_bytes, need);
   if (st != 0) return st < 0 ? st : TT_OK;
@@ -575,15 +654,15 @@ int launch(const void* q, const void* kb, const void* vb, const void* kc, const 
   a.q = (const T*)q; a.kb = (const T*)kb; a.vb = (const T*)vb;
   a.kc = (const T*)kc; a.vc = (const T*)vc;
   a.ctx_start = cs; a.ctx_len = cl; a.out = (T*)out;
-  a.ws_o = (float*)ws;
+  a.ws_o = (PartT<T>*)ws;
   a.ws_ml = (float2*)((char*)ws + o_bytes);
   a.B = B; a.S = S; a.Hq = Hq; a.Hkv = Hkv; a.ctx_rows = ctx_rows; a.W = W;
   a.c = scale * LOG2E;
   hipLaunchKernelGGL((attn_partial<T, D>), dim3(W), dim3(AT_THREADS), 0, stream, a);
   if (tt_launch_status() != TT_OK) return TT_ERR_HIP;
   if (W > 1) {
-    constexpr int RPB = AT_THREADS / (D / 4);
-    hipLaunchKernelGGL((attn_combine<T, D>), dim3((R + RPB - 1) / RPB, U), dim3(AT_THREADS), 0,
+    constexpr int RPB = CB_THREADS / (D / (16 / (int)sizeof(PartT<T>)));
+    hipLaunchKernelGGL((attn_combine<T, D>), dim3((R + RPB - 1) / RPB, U), dim3(CB_THREADS), 0,
                        stream, a);
     if (tt_launch_status() != TT_OK) return TT_ERR_HIP;
   }

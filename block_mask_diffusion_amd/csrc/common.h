@@ -41,6 +41,16 @@ static inline int tt_workspace_check(void* ws, size_t* ws_bytes, size_t need) {
 __device__ __forceinline__ float tt_shfl_xor(float v, int mask) { return __shfl_xor(v, mask, TT_WAVE); }
 __device__ __forceinline__ int tt_shfl_xor(int v, int mask) { return __shfl_xor(v, mask, TT_WAVE); }
 
+// Value of lane l ^ 32 (the other half of the wave) without an LDS round trip: one
+// v_permlane32_swap exchanges the upper half of its first operand with the lower half of its
+// second, so with both operands = v, lanes 0..31 find their partner in the second result and
+// lanes 32..63 in the first.
+__device__ __forceinline__ float tt_swap_halves(float v) {
+  const unsigned u = __float_as_uint(v);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
 // exp2 on the hardware transcendental unit (v_exp_f32): exact at 0, returns 0 for -inf.
 __device__ __forceinline__ float tt_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

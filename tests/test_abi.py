@@ -49,11 +49,14 @@ def test_attn_workspace_query_and_size():
     st, n = _attn()
     assert st == 0
     # 2 units, 4128 keys -> ceil(4128/128) = 33 workgroups; slots = 33 + 2, R = 256 rows, D = 128
+    # fp32 normalised partials + (m, l) as two fp32 per row
     slots, R, D = 35, 256, 128
     expect = -(-(slots * R * D * 4) // 256) * 256 + -(-(slots * R * 8) // 256) * 256
     assert n == expect
     st, n4 = _attn(B=4, max_prefix=131072, ctx_rows=4 * 131072)
     assert st == 0 and n4 == -(-((256 + 8) * R * D * 4) // 256) * 256 + -(-((256 + 8) * R * 8) // 256) * 256
+    st, nf = _attn(dtype=_lib.TT_F32)
+    assert st == 0 and nf == n
 
 
 @pytest.mark.parametrize("kw,code", [

@@ -107,3 +107,20 @@ def test_deterministic():
                               d["ctx_len"], max_prefix=wl.max_prefix) for _ in range(2)]
     torch.cuda.synchronize()
     assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+
+
+def test_extreme_scores_exercise_running_max():
+    """Q and K scaled by 8 (exact in bf16): scores spread over hundreds of units, so a wrong row
+    max (e.g. one wave half not seeing the other's maximum) or a missed rescale overflows the
+    exponentials and shows up as inf/NaN or a large error. The softmax is then nearly one-hot and
+    outputs approach single value rows; V is halved (exact) so that |o| stays below 4, where the
+    bf16 output rounding alone cannot exceed the 1e-2 bound."""
+    wl = _wl(1, B=3, prefixes=[700, 1500, 64])
+    wl.wid = 610
+    inp = synth.attn_inputs(wl)
+    for k, f in (("q", 8.0), ("k_blk", 8.0), ("k_ctx", 8.0), ("v_blk", 0.5), ("v_ctx", 0.5)):
+        inp[k] = synth.to_bf16_bits(oracle.decode(inp[k], "bf16").astype(np.float32) * f)
+    got = _run(inp, wl)
+    ref = oracle.block_attention(inp, wl.dtype)
+    assert np.all(np.isfinite(got))
+    assert float(np.max(np.abs(got - ref))) <= ATOL_BF16
