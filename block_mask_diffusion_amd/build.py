@@ -20,7 +20,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtt.so")
-SOURCES = ["attn.hip", "lmhead.hip", "unmask.hip", "api.hip"]
+SOURCES = ["attn.hip", "lmhead.hip", "gemm.hip", "unmask.hip", "api.hip"]
+# per-source extra flags: the large-M LM-head kernel keeps the next k-step's LDS reads in flight
+# under the current MFMAs only with the ILP-oriented machine scheduler
+EXTRA = {"gemm.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
 ARCH = os.environ.get("TT_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -44,7 +47,7 @@ def build(isa: bool = False, verbose: bool = False) -> str:
 
     def one(src):
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-        cmd = [HIPCC, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC, *CFLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
         if isa:
             cmd += ["-save-temps=obj"]
         out = _run(cmd)

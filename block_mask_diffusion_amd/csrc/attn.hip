@@ -193,39 +193,7 @@ struct Args {
   float c;  // softmax_scale * log2(e)
 };
 
-template <int N>
-__device__ __forceinline__ void wait_vmem() {  // this wave's oldest outstanding VMEM ops, all but N
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
-
-// LDS byte address of a __shared__ location, made wave-uniform (it goes to M0).
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)LDS_PTR(const void, p));
-}
-
-// Direct global->LDS load of 16 bytes per lane: lane i's bytes land at LDS address base + 16 i.
-// Written as inline asm on purpose: the compiler then does not track these writes to LDS, so it
-// does not put a wait for every outstanding global load in front of each LDS read of the ring.
-// Ordering is explicit instead: each stage's readers wait (counted vmcnt, then a barrier) for
-// that stage's loads only, and a buffer is refilled only after the barrier that ends its reads.
-// M0 (which holds the LDS base) is saved to a scratch SGPR and restored inside the same asm, so
-// the compiler's own use of M0 is unaffected. The only register output is that scratch SGPR,
-// written by a scalar move; the load itself returns nothing to registers.
-__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"  // one wait state between an SALU write of M0 and its use by an LDS DMA
-      "global_load_lds_dwordx4 %1, off\n\t"
-      "s_nop 0\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(gptr), "s"(lds_base)
-      : "memory");
-}
+#define LDS_PTR(T, p) TT_LDS_PTR(T, p)
 
 template <typename T, int D>
 __global__ __launch_bounds__(AT_THREADS, 1) void attn_partial(Args<T, D> A) {
@@ -332,17 +300,17 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_partial(Args<T, D> A) {
         const int gk = slot ^ GE::fk(r), gv = slot ^ GE::fv(r);
         const T* kp = key < P ? kctx + (size_t)key * D : kblk + (size_t)(key - P) * blk_stride;
         const T* vp = key < P ? vctx + (size_t)key * D : vblk + (size_t)(key - P) * blk_stride;
-        dma16(reinterpret_cast<const unsigned char*>(kp) + 16 * gk, lds_addr(&ring.k[buf][chunk * 1024]));
-        dma16(reinterpret_cast<const unsigned char*>(vp) + 16 * gv, lds_addr(&ring.v[buf][chunk * 1024]));
+        tt_dma16(reinterpret_cast<const unsigned char*>(kp) + 16 * gk, tt_lds_addr(&ring.k[buf][chunk * 1024]));
+        tt_dma16(reinterpret_cast<const unsigned char*>(vp) + 16 * gv, tt_lds_addr(&ring.v[buf][chunk * 1024]));
       }
     };
     // stage st resident: wait for this wave's loads of stage st (the later stages stay in flight),
     // then a barrier so every wave's loads of stage st are in LDS
     auto stage_ready = [&](int st, int nst) {
       const int later = min(nst - 1, st + NBUF - 2) - st;  // stages issued after st
-      if (later >= 2) wait_vmem<2 * GE::DPW>();
-      else if (later == 1) wait_vmem<GE::DPW>();
-      else wait_vmem<0>();
+      if (later >= 2) tt_wait_vmem<2 * GE::DPW>();
+      else if (later == 1) tt_wait_vmem<GE::DPW>();
+      else tt_wait_vmem<0>();
       tt_lds_barrier();
     };
 
@@ -402,7 +370,7 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_partial(Args<T, D> A) {
     };
 
     const int nst = (nkeys + KC - 1) / KC;
-    wait_vmem<0>();   // the previous piece's partial stores; the load counting below starts clean
+    tt_wait_vmem<0>();   // the previous piece's partial stores; the load counting below starts clean
     __syncthreads();  // previous piece's readers are done with the ring
 #pragma unroll
     for (int st = 0; st < NBUF - 1; ++st)

@@ -61,3 +61,39 @@ __device__ __forceinline__ float tt_exp2(float x) { return __builtin_amdgcn_exp2
 __device__ __forceinline__ void tt_lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
+
+// Wait until at most N of this wave's vector-memory operations are outstanding (they complete
+// in issue order).
+template <int N>
+__device__ __forceinline__ void tt_wait_vmem() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+#define TT_LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+// LDS byte address of a __shared__ location, made wave-uniform (it goes to M0).
+__device__ __forceinline__ uint32_t tt_lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)TT_LDS_PTR(const void, p));
+}
+
+// Direct global->LDS load of 16 bytes per lane: lane i's bytes land at LDS address base + 16 i.
+// Written as inline asm on purpose: the compiler then does not track these writes to LDS, so it
+// does not put a wait for every outstanding global load in front of each LDS read of a ring
+// that such loads fill. Ordering is the caller's job instead: each stage's readers wait (counted
+// vmcnt, then a barrier) for that stage's loads only, and a buffer is refilled only after the
+// barrier that ends its reads. M0 (which holds the LDS base) is saved to a scratch SGPR and
+// restored inside the same asm, so the compiler's own use of M0 is unaffected. The only register
+// output is that scratch SGPR, written by a scalar move; the load returns nothing to registers.
+__device__ __forceinline__ void tt_dma16(const void* gptr, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"  // one wait state between an SALU write of M0 and its use by an LDS DMA
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_nop 0\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(gptr), "s"(lds_base)
+      : "memory");
+}

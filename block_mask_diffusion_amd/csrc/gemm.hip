@@ -1,0 +1,168 @@
+// LM-head product for many hidden rows (M > 128), where it is bound by the matrix cores rather
+// than by streaming W ("Nemotron-Labs-TwoTower" wiki page, section "Block-wise generation": every
+// denoising step predicts all masked positions of every block in parallel).
+//
+// Built with the iterative ILP machine scheduler (see build.py): with one wave per SIMD the
+// kernel relies on the next k-step's LDS reads being in flight while the current MFMAs run,
+// which the default occupancy-oriented schedule undoes by sinking each read next to its use.
+#include "lmhead_int.h"
+
+namespace {
+
+constexpr int LM_THREADS = 256;
+constexpr int LM_WAVES = 4;
+constexpr int NXCD = 8;
+// v_mfma_f32_32x32x16_bf16 result layout (lane l, register j): column l % 32,
+// row 8 (j / 4) + 4 (l / 32) + j % 4
+__device__ __forceinline__ int mrow(int lane, int j) { return 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3); }
+
+// Workgroup = 4 waves, each owning a 128 x 128 block of 4 x 4 MFMA 32x32x16 tiles (256
+// accumulators per lane, held in AGPRs; one wave per SIMD). Both operands go HBM/L2 -> LDS by
+// direct loads into a 2-deep ring of GM_KB = 64-wide k stages: each row contributes one whole
+// 128-byte line per stage, and the next stage's loads run while the current one is multiplied.
+// LDS -> registers in MFMA operand layout: a lane reads 16 bytes = 8 consecutive h of one row;
+// the 16-byte granules of row r are stored at slot g ^ ((r >> 1) & 7), so the 16 rows read by
+// 16 consecutive lanes hit 16 distinct 16-byte bank groups. The next k-step's fragments are read
+// while the current k-step's MFMAs run. The default tile is 256 hidden rows x 256 vocabulary
+// rows (2 x 2 waves); with two hidden-row blocks the workgroups of one vocabulary tile have
+// dispatch ids congruent modulo 8 (same XCD) and 8 apart, so W is fetched from HBM once (measured
+// with FETCH_SIZE). A 512 x 128 tile (W read by one workgroup only) measured slower: it doubles
+// the re-reads of the hidden rows from L2.
+constexpr int GM_KB = TT_GEMM_KB, GM_NBUF = 2;
+constexpr int GM_ROWB = GM_KB * 2;                  // bytes per LDS row (one cache line)
+constexpr int GM_KS = GM_KB / 16;                   // MFMA k-steps per stage
+static_assert(GM_ROWB == 128, "ring geometry");
+
+__device__ __forceinline__ int gm_swz(int r) { return (r >> 1) & 7; }
+
+// WM waves along the hidden rows, 4 / WM along the vocabulary, each owning a 128 x 128 block:
+// tile BM = 128 WM hidden rows x BN = 128 (4 / WM) vocabulary rows.
+template <int WM>
+__global__ __launch_bounds__(LM_THREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void lmhead_gemm_kernel(
+    const bf16* __restrict__ hidden, const bf16* __restrict__ w, float* __restrict__ logits, int M, int H,
+    int V, int nvt, int nmb) {
+  constexpr int WN = LM_WAVES / WM;
+  constexpr int GM_BM = 128 * WM, GM_BN = 128 * WN;
+  constexpr int ASTAGE = GM_BM * GM_ROWB, BSTAGE = GM_BN * GM_ROWB;  // bytes per stage
+  constexpr int ACPW = ASTAGE / 1024 / LM_WAVES, BCPW = BSTAGE / 1024 / LM_WAVES;  // chunks per wave
+  typedef bf16x8 frag;
+  __shared__ __attribute__((aligned(16))) unsigned char sa[GM_NBUF][ASTAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char sb[GM_NBUF][BSTAGE];
+  static_assert(GM_NBUF * (ASTAGE + BSTAGE) <= 160 * 1024, "LDS per workgroup");
+
+  const int id = blockIdx.x;
+  const int grp = id / (NXCD * nmb);
+  const int rem = id - grp * NXCD * nmb;
+  const int mblk = rem / NXCD;
+  const int vtile = grp * NXCD + rem % NXCD;
+  if (vtile >= nvt) return;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int wm = wave / WN, wn = wave % WN;
+  const int m0 = mblk * GM_BM, v0 = vtile * GM_BN;
+
+  // load sources: chunk c = wave * CPW + i covers tile rows [8c, 8c + 8); lane -> row
+  // 8c + lane / 8, LDS slot lane % 8, which holds logical granule slot ^ swz(row). Rows past M
+  // or V re-read the last row (in bounds; their results are never stored).
+  const bf16* asrc[ACPW];
+  const bf16* bsrc[BCPW];
+#pragma unroll
+  for (int i = 0; i < ACPW; ++i) {
+    const int r = (wave * ACPW + i) * 8 + lane / 8;
+    asrc[i] = hidden + (size_t)min(m0 + r, M - 1) * H + 8 * ((lane & 7) ^ gm_swz(r));
+  }
+#pragma unroll
+  for (int i = 0; i < BCPW; ++i) {
+    const int r = (wave * BCPW + i) * 8 + lane / 8;
+    bsrc[i] = w + (size_t)min(v0 + r, V - 1) * H + 8 * ((lane & 7) ^ gm_swz(r));
+  }
+  auto issue = [&](int st) {
+    const int buf = st % GM_NBUF, k0 = st * GM_KB;
+#pragma unroll
+    for (int i = 0; i < ACPW; ++i) tt_dma16(asrc[i] + k0, tt_lds_addr(&sa[buf][(wave * ACPW + i) * 1024]));
+#pragma unroll
+    for (int i = 0; i < BCPW; ++i) tt_dma16(bsrc[i] + k0, tt_lds_addr(&sb[buf][(wave * BCPW + i) * 1024]));
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[mt][nt][j] = 0.f;
+
+  // fragments of k-step ks of the stage in buffer buf
+  auto read_frags = [&](int buf, int ks, frag (&fa)[4], frag (&fb)[4]) {
+    const unsigned char* a_s = sa[buf];
+    const unsigned char* b_s = sb[buf];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int ra = 128 * wm + 32 * t + l32, rb = 128 * wn + 32 * t + l32;
+      const int gsl = 2 * ks + hh;
+      fa[t] = *reinterpret_cast<const frag*>(a_s + ra * GM_ROWB + 16 * (gsl ^ gm_swz(ra)));
+      fb[t] = *reinterpret_cast<const frag*>(b_s + rb * GM_ROWB + 16 * (gsl ^ gm_swz(rb)));
+    }
+  };
+  auto mma_step = [&](const frag (&fa)[4], const frag (&fb)[4]) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+        acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mt], fb[nt], acc[mt][nt], 0, 0, 0);
+  };
+
+  // Stage st: wait for this wave's loads of it (the only ones outstanding), barrier (every
+  // wave's loads are in LDS and stage st - 1 has been read by all), refill the other buffer with
+  // stage st + 1, then 4 k-steps with the fragments of step ks + 1 read during step ks.
+  // Stage st: wait for this wave's loads of it (the only ones outstanding), barrier (every
+  // wave's loads are in LDS and stage st - 1 has been read by all), refill the other buffer with
+  // stage st + 1, then GM_KS k-steps with the fragments of step ks + 1 read during step ks.
+  const int nst = H / GM_KB;
+  issue(0);
+  for (int st = 0; st < nst; ++st) {
+    tt_wait_vmem<0>();
+    tt_lds_barrier();
+    if (st + 1 < nst) issue(st + 1);
+    const int buf = st % GM_NBUF;
+    frag fa0[4], fb0[4], fa1[4], fb1[4];
+    read_frags(buf, 0, fa0, fb0);
+#pragma unroll
+    for (int ks = 0; ks < GM_KS; ks += 2) {
+      read_frags(buf, ks + 1, fa1, fb1);
+      mma_step(fa0, fb0);
+      if (ks + 2 < GM_KS) read_frags(buf, ks + 2, fa0, fb0);
+      mma_step(fa1, fb1);
+    }
+  }
+
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int v = v0 + 128 * wn + 32 * nt + l32;
+      if (v >= V) continue;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int m = m0 + 128 * wm + 32 * mt + mrow(lane, j);
+        if (m < M) logits[(size_t)m * V + v] = acc[mt][nt][j];
+      }
+    }
+}
+
+}  // namespace
+
+#ifndef TT_GEMM_WM
+#define TT_GEMM_WM 2
+#endif
+
+int tt_lm_gemm_launch(const void* hidden, const void* w, float* logits, int M, int H, int V, hipStream_t s) {
+  constexpr int WM = TT_GEMM_WM, BM = 128 * WM, BN = 128 * (LM_WAVES / WM);
+  const int nvt = (V + BN - 1) / BN;
+  const int nmb = (M + BM - 1) / BM;
+  const unsigned grid = (unsigned)(((nvt + NXCD - 1) / NXCD) * NXCD * nmb);
+  hipLaunchKernelGGL(lmhead_gemm_kernel<WM>, dim3(grid), dim3(LM_THREADS), 0, s, (const bf16*)hidden,
+                     (const bf16*)w, logits, M, H, V, nvt, nmb);
+  return tt_launch_status();
+}

@@ -19,7 +19,7 @@
 //
 // When M needs several hidden-row blocks, the workgroups of one vocabulary tile are placed on the
 // same XCD (dispatch ids congruent modulo 8 land on the same XCD), so the blocks share W in L2.
-#include "common.h"
+#include "lmhead_int.h"
 
 namespace {
 
@@ -434,6 +434,7 @@ int lm_bf16(const void* h, const void* w, float* o, int M, int H, int V, hipStre
   else if (M <= 64) st = lm_try_lds<TT_LM_LDS64>(h, w, o, M, H, V, s);
   else if (M <= 128) st = lm_try_lds<TT_LM_LDS128>(h, w, o, M, H, V, s);
   if (st != 1) return st;
+  if (M > 128 && H % TT_GEMM_KB == 0) return tt_lm_gemm_launch(h, w, o, M, H, V, s);
   if (M <= 32) return lm_direct<TT_LM_CFG32>(h, w, o, M, H, V, s);
   if (M <= 64) return lm_direct<TT_LM_CFG64>(h, w, o, M, H, V, s);
   return lm_direct<TT_LM_CFGBIG>(h, w, o, M, H, V, s);
