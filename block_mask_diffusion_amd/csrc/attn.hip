@@ -99,6 +99,7 @@ struct Mf<float> {
 template <typename T>
 constexpr int kc_of() { return sizeof(T) == 2 ? 64 : 32; }
 constexpr int NBUF = 4;
+constexpr int PD = NBUF - 1;  // stages whose loads run ahead
 
 template <typename T, int D>
 struct Geo {
@@ -283,31 +284,53 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_partial(Args<T, D> A) {
         for (int j = 0; j < 16; ++j) o[t][dt][j] = 0.f;
     }
 
-    // ---- stage loads: global -> LDS directly. Chunk c of a stage holds rows [c*RPC, c*RPC+RPC);
-    // lane i writes LDS bytes [16i, 16i+16) of the chunk = granule slot i%GPR of row i/GPR, which
-    // holds logical granule slot ^ f(row). Keys past the piece end re-read its last key (their
-    // scores are masked and their probabilities are exactly 0).
+    // ---- stage loads: global -> LDS directly
     const int nkeys = ke - ka;
-    auto issue_stage = [&](int st) {
+    // Per-lane load sources of this piece. Chunk c of a stage holds rows [c*RPC, c*RPC+RPC); lane i
+    // writes LDS bytes [16i, 16i+16) of the chunk = granule slot i%GPR of row i/GPR, which holds
+    // logical granule slot ^ f(row); the row and so the swizzle are the same in every stage.
+    // Fast path (uniform per stage): all KC keys of the stage are context keys of this piece, so
+    // each source is the piece's first stage address plus st * KC rows. Otherwise each key is
+    // clamped to the piece and taken from the context or the block rows; keys past the piece end
+    // re-read its last key (their scores are masked and their probabilities are exactly 0).
+    const unsigned char* kfast[CPW];
+    const unsigned char* vfast[CPW];
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      const int r = (wave * CPW + c) * GE::RPC + lane / GPR, slot = lane % GPR;
+      kfast[c] = reinterpret_cast<const unsigned char*>(kctx + (size_t)(ka + r) * D) + 16 * (slot ^ GE::fk(r));
+      vfast[c] = reinterpret_cast<const unsigned char*>(vctx + (size_t)(ka + r) * D) + 16 * (slot ^ GE::fv(r));
+    }
+    const int fast_end = min(P, ke);  // keys below this are context keys of the piece
+    // one load of stage st: chunk c of K (kv = 0) or of V (kv = 1)
+    auto issue_chunk = [&](int st, int c, int kv) {
       const int buf = st % NBUF;
       const int k0 = ka + st * KC;
+      const int chunk = wave * CPW + c;
+      unsigned char* dst = kv ? &ring.v[buf][chunk * 1024] : &ring.k[buf][chunk * 1024];
+      if (k0 + KC <= fast_end) {
+        tt_dma16((kv ? vfast[c] : kfast[c]) + (size_t)st * KC * RB, tt_lds_addr(dst));
+        return;
+      }
+      const int r = chunk * GE::RPC + lane / GPR, slot = lane % GPR;
+      int key = k0 + r;
+      key = key < ke ? key : ke - 1;
+      const int g = slot ^ (kv ? GE::fv(r) : GE::fk(r));
+      const T* src = kv ? (key < P ? vctx + (size_t)key * D : vblk + (size_t)(key - P) * blk_stride)
+                        : (key < P ? kctx + (size_t)key * D : kblk + (size_t)(key - P) * blk_stride);
+      tt_dma16(reinterpret_cast<const unsigned char*>(src) + 16 * g, tt_lds_addr(dst));
+    };
+    auto issue_stage = [&](int st) {
 #pragma unroll
       for (int c = 0; c < CPW; ++c) {
-        const int chunk = wave * CPW + c;
-        const int r = chunk * GE::RPC + lane / GPR, slot = lane % GPR;
-        int key = k0 + r;
-        key = key < ke ? key : ke - 1;
-        const int gk = slot ^ GE::fk(r), gv = slot ^ GE::fv(r);
-        const T* kp = key < P ? kctx + (size_t)key * D : kblk + (size_t)(key - P) * blk_stride;
-        const T* vp = key < P ? vctx + (size_t)key * D : vblk + (size_t)(key - P) * blk_stride;
-        tt_dma16(reinterpret_cast<const unsigned char*>(kp) + 16 * gk, tt_lds_addr(&ring.k[buf][chunk * 1024]));
-        tt_dma16(reinterpret_cast<const unsigned char*>(vp) + 16 * gv, tt_lds_addr(&ring.v[buf][chunk * 1024]));
+        issue_chunk(st, c, 0);
+        issue_chunk(st, c, 1);
       }
     };
     // stage st resident: wait for this wave's loads of stage st (the later stages stay in flight),
     // then a barrier so every wave's loads of stage st are in LDS
     auto stage_ready = [&](int st, int nst) {
-      const int later = min(nst - 1, st + NBUF - 2) - st;  // stages issued after st
+      const int later = min(nst - 1, st + PD - 1) - st;  // stages issued after st
       if (later >= 2) tt_wait_vmem<2 * GE::DPW>();
       else if (later == 1) tt_wait_vmem<GE::DPW>();
       else tt_wait_vmem<0>();
@@ -369,78 +392,87 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_partial(Args<T, D> A) {
       }
     };
 
+    // softmax of one sub-tile's scores (in place) -> bf16/fp32 probabilities pf; updates the
+    // running max (lazy rescale of o and l) and the running sum l
+    auto softmax = [&](f32x16 (&sacc)[TPW], int kvalid, frag (&pf)[TPW][32 / KS]) {
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        if (kvalid < 32) {
+#pragma unroll
+          for (int j = 0; j < 16; ++j)
+            if (8 * (j >> 2) + 4 * hh2 + (j & 3) >= kvalid) sacc[t][j] = -INFINITY;
+        }
+        float mx = fmaxf(fmaxf(sacc[t][0], sacc[t][1]), sacc[t][2]);
+#pragma unroll
+        for (int j = 3; j < 15; j += 2) mx = fmaxf(fmaxf(mx, sacc[t][j]), sacc[t][j + 1]);
+        mx = fmaxf(mx, sacc[t][15]);
+        mx = fmaxf(mx, tt_swap_halves(mx));
+        // Lazy rescale: the reference max only moves when a row's max grows by more than
+        // 2^8 in the exponent; exponentials stay <= 256 and the final normalisation is exact.
+        if (__ballot((mx - mrun[t]) * A.c > RESCALE_LOG2)) {
+          const float mnew = fmaxf(mrun[t], mx);
+          const float alpha = tt_exp2((mrun[t] - mnew) * A.c);  // 0 on the first update
+          lrun[t] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) o[t][dt][j] *= alpha;
+          mrun[t] = mnew;
+        }
+        const float mc = mrun[t] * A.c;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) sacc[t][j] = tt_exp2(fmaf(sacc[t][j], A.c, -mc));
+#pragma unroll
+        for (int uu = 0; uu < 32 / KS; ++uu) pf[t][uu] = MF::pfrag(sacc[t], uu);
+        // row sum of the probabilities exactly as the PV product uses them
+        lrun[t] = MF::psum(pf[t], sacc[t], lrun[t]);
+      }
+    };
+    auto vread = [&](const unsigned char* vb_, int kt, frag (&va)[D / 32][32 / KS]) {
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int uu = 0; uu < 32 / KS; ++uu) va[dt][uu] = vfrag(vb_, kt, uu, dt);
+    };
+    auto pv = [&](const frag (&va)[D / 32][32 / KS], const frag (&pf)[TPW][32 / KS]) {
+      if (TT_AT_PRIO) __builtin_amdgcn_s_setprio(2);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int uu = 0; uu < 32 / KS; ++uu)
+#pragma unroll
+          for (int t = 0; t < TPW; ++t) o[t][dt] = MF::mma(va[dt][uu], pf[t][uu], o[t][dt]);
+      if (TT_AT_PRIO) __builtin_amdgcn_s_setprio(0);
+    };
+
     const int nst = (nkeys + KC - 1) / KC;
     tt_wait_vmem<0>();   // the previous piece's partial stores; the load counting below starts clean
     __syncthreads();  // previous piece's readers are done with the ring
 #pragma unroll
-    for (int st = 0; st < NBUF - 1; ++st)
+    for (int st = 0; st < PD; ++st)
       if (st < nst) issue_stage(st);
 
+    // one sub-tile: scores, softmax, and (unless deferred) the PV product
+    // one sub-tile: scores, softmax and the PV product
+    auto subtile = [&](int st, int kt) {
+      const int kvalid = nkeys - st * KC - kt * 32;  // keys of this sub-tile that exist
+      frag kf[D / KS];
+      kread(ring.k[st % NBUF], kt, kf);
+      f32x16 sacc[TPW];
+      qk(kf, sacc);
+      frag pf[TPW][32 / KS];
+      softmax(sacc, kvalid, pf);
+      frag va[D / 32][32 / KS];
+      vread(ring.v[st % NBUF], kt, va);
+      pv(va, pf);
+    };
     for (int st = 0; st < nst; ++st) {
-      stage_ready(st, nst);                                  // B_st
-      if (st + NBUF - 1 < nst) issue_stage(st + NBUF - 1);   // into the buffer of stage st-1
-      const unsigned char* kbuf = ring.k[st % NBUF];
-      const unsigned char* vbuf = ring.v[st % NBUF];
-      if (active) {
+      stage_ready(st, nst);                       // B_st
+      if (st + PD < nst) issue_stage(st + PD);    // into the buffer of stage st - 1
+      if (!active) continue;
 #pragma unroll
-        for (int kt = 0; kt < SPS; ++kt) {
-          const int kvalid = nkeys - st * KC - kt * 32;  // keys of this sub-tile that exist
-          if (kvalid > 0) {
-            frag kf[D / KS];
-            kread(kbuf, kt, kf);
-            f32x16 sacc[TPW];
-            qk(kf, sacc);
-            // V^T fragments of the whole sub-tile, issued now so that their LDS latency is
-            // hidden behind the softmax below (they do not depend on it)
-            frag va[D / 32][32 / KS];
-#pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-              for (int uu = 0; uu < 32 / KS; ++uu) va[dt][uu] = vfrag(vbuf, kt, uu, dt);
-            frag pf[TPW][32 / KS];
-#pragma unroll
-            for (int t = 0; t < TPW; ++t) {
-              if (kvalid < 32) {
-#pragma unroll
-                for (int j = 0; j < 16; ++j)
-                  if (8 * (j >> 2) + 4 * hh2 + (j & 3) >= kvalid) sacc[t][j] = -INFINITY;
-              }
-              float mx = fmaxf(fmaxf(sacc[t][0], sacc[t][1]), sacc[t][2]);
-#pragma unroll
-              for (int j = 3; j < 15; j += 2) mx = fmaxf(fmaxf(mx, sacc[t][j]), sacc[t][j + 1]);
-              mx = fmaxf(mx, sacc[t][15]);
-              mx = fmaxf(mx, tt_swap_halves(mx));
-              // Lazy rescale: the reference max only moves when a row's max grows by more than
-              // 2^8 in the exponent; exponentials stay <= 256 and the final normalisation is exact.
-              if (__ballot((mx - mrun[t]) * A.c > RESCALE_LOG2)) {
-                const float mnew = fmaxf(mrun[t], mx);
-                const float alpha = tt_exp2((mrun[t] - mnew) * A.c);  // 0 on the first update
-                lrun[t] *= alpha;
-#pragma unroll
-                for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-                  for (int j = 0; j < 16; ++j) o[t][dt][j] *= alpha;
-                mrun[t] = mnew;
-              }
-              const float mc = mrun[t] * A.c;
-#pragma unroll
-              for (int j = 0; j < 16; ++j) sacc[t][j] = tt_exp2(fmaf(sacc[t][j], A.c, -mc));
-#pragma unroll
-              for (int uu = 0; uu < 32 / KS; ++uu) pf[t][uu] = MF::pfrag(sacc[t], uu);
-              // row sum of the probabilities exactly as the PV product uses them
-              lrun[t] = MF::psum(pf[t], sacc[t], lrun[t]);
-            }
-            if (TT_AT_PRIO) __builtin_amdgcn_s_setprio(2);
-#pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-              for (int uu = 0; uu < 32 / KS; ++uu)
-#pragma unroll
-                for (int t = 0; t < TPW; ++t) o[t][dt] = MF::mma(va[dt][uu], pf[t][uu], o[t][dt]);
-            if (TT_AT_PRIO) __builtin_amdgcn_s_setprio(0);
-          }
-        }
-      }
+      for (int kt = 0; kt < SPS; ++kt)
+        if (nkeys - st * KC - kt * 32 > 0) subtile(st, kt);
     }
 
     // ---- epilogue: direct normalised output, or a normalised partial in slot w + u
