@@ -130,15 +130,17 @@ struct alignas(16) Ring {
   unsigned char v[NBUF][Geo<T, D>::STAGE];
 };
 
+template <int NT>
 struct Scan {
   int pb[AT_MAX_B + 1];  // pb[b] = sum_{b' < b} (ctx_len[b'] + S)
-  int tmp[AT_THREADS];
+  int tmp[NT];
 };
 
-// Exclusive prefix sums of N_b = ctx_len[b] + S into sc.pb[0..B] (B <= AT_MAX_B).
-__device__ void scan_lengths(Scan& sc, const int32_t* __restrict__ ctx_len, int B, int S) {
+// Exclusive prefix sums of N_b = ctx_len[b] + S into sc.pb[0..B] (B <= AT_MAX_B), NT threads.
+template <int NT>
+__device__ void scan_lengths(Scan<NT>& sc, const int32_t* __restrict__ ctx_len, int B, int S) {
   const int t = threadIdx.x;
-  constexpr int PER = AT_MAX_B / AT_THREADS;
+  constexpr int PER = AT_MAX_B / NT;
   int v[PER];
   int loc = 0;
 #pragma unroll
@@ -149,7 +151,7 @@ __device__ void scan_lengths(Scan& sc, const int32_t* __restrict__ ctx_len, int 
   }
   sc.tmp[t] = loc;
   __syncthreads();
-  for (int off = 1; off < AT_THREADS; off <<= 1) {  // Hillis-Steele inclusive scan
+  for (int off = 1; off < NT; off <<= 1) {  // Hillis-Steele inclusive scan
     int x = (t >= off) ? sc.tmp[t - off] : 0;
     __syncthreads();
     sc.tmp[t] += x;
@@ -161,7 +163,7 @@ __device__ void scan_lengths(Scan& sc, const int32_t* __restrict__ ctx_len, int 
     sc.pb[t * PER + k] = run;
     run += v[k];
   }
-  if (t == AT_THREADS - 1) sc.pb[AT_MAX_B] = run;
+  if (t == NT - 1) sc.pb[AT_MAX_B] = run;
   __syncthreads();
 }
 
@@ -206,7 +208,7 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_partial(Args<T, D> A) {
   constexpr int CPW = GE::NCH / AT_WAVES;       // K (and V) chunks per wave per stage
 
   __shared__ Ring<T, D> ring;
-  __shared__ Scan sc;
+  __shared__ Scan<AT_THREADS> sc;
 
   const int tid = threadIdx.x;
   const int lane = tid & (TT_WAVE - 1);
@@ -219,7 +221,7 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_partial(Args<T, D> A) {
   const int U = A.B * A.Hkv;
   const bool active = wave * TPW * QT < R;  // this wave owns query rows [32*TPW*wave, +32*TPW)
 
-  scan_lengths(sc, A.ctx_len, A.B, A.S);
+  scan_lengths<AT_THREADS>(sc, A.ctx_len, A.B, A.S);
   const int64_t Ttot = (int64_t)A.Hkv * sc.pb[A.B];
   const int64_t lo = (int64_t)w * Ttot / A.W;
   const int64_t hi = (int64_t)(w + 1) * Ttot / A.W;
@@ -552,18 +554,25 @@ __device__ __forceinline__ void block_sum2(int64_t& a, int64_t& b) {
   }
 }
 
-// Split-K merge of one unit's normalised partials, in workgroup order (fixed, so the result is
-// reproducible): O = sum_k e^(m_k - M) l_k Ohat_k / sum_k e^(m_k - M) l_k. Each thread owns VPT
-// consecutive output elements of one query row (one 16-byte load per partial).
-template <typename T, int D>
+// Split-K merge of a unit's normalised partials: O = sum_k e^(m_k - M) l_k Ohat_k /
+// sum_k e^(m_k - M) l_k. Workgroup = RPB query rows of one unit; thread (row rr, group sg, part
+// tr) owns VPT consecutive output elements of its row and the partials of workgroups wf + sg,
+// wf + sg + NSG, ... (CB loads in flight together); the NSG groups of a row are merged in the
+// order sg = 0, 1, ... through LDS, a fixed order, so the result is reproducible. Many partials
+// per unit (long sequences) use several groups per row, few partials several rows per group.
+template <typename T, int D, int NSG>
 __global__ __launch_bounds__(CB_THREADS) void attn_combine(Args<T, D> A) {
   typedef PartT<T> PT;
-  constexpr int VPT = 16 / (int)sizeof(PT);  // elements per thread
-  constexpr int TPR = D / VPT;               // threads per query row
-  constexpr int RPB = CB_THREADS / TPR;      // rows per workgroup
+  constexpr int VPT = 16 / (int)sizeof(PT);  // elements per thread (one 16-byte load)
+  constexpr int TPR = D / VPT;               // threads per row part
+  constexpr int RPB = CB_THREADS / (TPR * NSG);  // rows per workgroup
+  static_assert(RPB >= 1 && RPB * TPR * NSG == CB_THREADS, "combine geometry");
+  constexpr int CB = 8;                      // partials per group whose loads are in flight together
   const int G = A.Hq / A.Hkv;
   const int R = A.S * G;
-  const int u = blockIdx.y;
+  const int u = blockIdx.x;    // unit on x (up to B * Hkv workgroups), row block on y
+  const int rr = threadIdx.x / (TPR * NSG);
+  const int row = blockIdx.y * RPB + rr;
   const int bb = u / A.Hkv, g = u - bb * A.Hkv;
   // key-space offsets: sum of N_b' = ctx_len[b'] + S over b' < bb, and over all b'
   int64_t before = 0, total = 0;
@@ -573,26 +582,26 @@ __global__ __launch_bounds__(CB_THREADS) void attn_combine(Args<T, D> A) {
     if (b2 < bb) before += n;
   }
   block_sum2(before, total);
-  const int row = blockIdx.x * RPB + threadIdx.x / TPR;
-  const int d = (threadIdx.x % TPR) * VPT;
-  if (row >= R) return;
   const int64_t Ttot = (int64_t)A.Hkv * total;
   const int N = A.ctx_len[bb] + A.S;
   const int64_t Ou = (int64_t)A.Hkv * before + (int64_t)g * N;
   const int wf = owner_of(Ou, Ttot, A.W), wl = owner_of(Ou + N - 1, Ttot, A.W);
   if (wf == wl) return;  // one workgroup held the whole unit and wrote the output itself
-  constexpr int CB = 8;  // partials whose loads are in flight together
+  const int sg = (threadIdx.x / TPR) % NSG, tr = threadIdx.x % TPR;
+  const bool live = row < R;
+  const int d = tr * VPT;
   float M = -INFINITY, L = 0.f;
   float acc[VPT];
 #pragma unroll
   for (int e = 0; e < VPT; ++e) acc[e] = 0.f;
-  for (int w0 = wf; w0 <= wl; w0 += CB) {
+  for (int w0 = wf + sg; live && w0 <= wl; w0 += NSG * CB) {
     float2 ml[CB];
     u32x4 ov[CB];
 #pragma unroll
     for (int k = 0; k < CB; ++k) {
-      const size_t slot = (size_t)(w0 + k) + u;
-      if (w0 + k <= wl) {
+      const int wk = w0 + NSG * k;
+      const size_t slot = (size_t)wk + u;
+      if (wk <= wl) {
         ml[k] = A.ws_ml[slot * R + row];
         ov[k] = *reinterpret_cast<const u32x4*>(A.ws_o + (slot * R + row) * D + d);
       } else {
@@ -617,6 +626,28 @@ __global__ __launch_bounds__(CB_THREADS) void attn_combine(Args<T, D> A) {
     }
     M = bm;
   }
+  if constexpr (NSG > 1) {
+    __shared__ float gm[RPB][NSG][TPR], gl[RPB][NSG][TPR];
+    __shared__ float ga[RPB][NSG][TPR][VPT];
+    gm[rr][sg][tr] = M;
+    gl[rr][sg][tr] = L;
+#pragma unroll
+    for (int e = 0; e < VPT; ++e) ga[rr][sg][tr][e] = acc[e];
+    __syncthreads();
+    if (sg != 0) return;
+    for (int q = 1; q < NSG; ++q) {
+      const float m2 = gm[rr][q][tr];
+      if (m2 == -INFINITY) continue;
+      const float bm = fmaxf(M, m2);
+      const float r1 = (M == -INFINITY) ? 0.f : tt_exp2((M - bm) * A.c);
+      const float r2 = tt_exp2((m2 - bm) * A.c);
+      L = L * r1 + gl[rr][q][tr] * r2;
+#pragma unroll
+      for (int e = 0; e < VPT; ++e) acc[e] = acc[e] * r1 + ga[rr][q][tr][e] * r2;
+      M = bm;
+    }
+  }
+  if (!live) return;
   const float inv = 1.f / L;
   const int s = row / G, hq = g * G + row % G;
   T* op = A.out + (((size_t)bb * A.S + s) * A.Hq + hq) * D + d;
@@ -661,9 +692,16 @@ int launch(const void* q, const void* kb, const void* vb, const void* kc, const 
   hipLaunchKernelGGL((attn_partial<T, D>), dim3(W), dim3(AT_THREADS), 0, stream, a);
   if (tt_launch_status() != TT_OK) return TT_ERR_HIP;
   if (W > 1) {
-    constexpr int RPB = CB_THREADS / (D / (16 / (int)sizeof(PartT<T>)));
-    hipLaunchKernelGGL((attn_combine<T, D>), dim3((R + RPB - 1) / RPB, U), dim3(CB_THREADS), 0,
-                       stream, a);
+    // slot groups per row: enough to cover a unit's partials (about W / U + 1) in one batch
+    constexpr int TPR = D / (16 / (int)sizeof(PartT<T>));
+    constexpr int NSG_MAX = CB_THREADS / TPR;
+    if (W / U + 1 >= 16) {
+      hipLaunchKernelGGL((attn_combine<T, D, NSG_MAX>), dim3(U, R), dim3(CB_THREADS), 0, stream, a);
+    } else {
+      constexpr int RPB = CB_THREADS / TPR;
+      hipLaunchKernelGGL((attn_combine<T, D, 1>), dim3(U, (R + RPB - 1) / RPB), dim3(CB_THREADS), 0,
+                         stream, a);
+    }
     if (tt_launch_status() != TT_OK) return TT_ERR_HIP;
   }
   return TT_OK;
