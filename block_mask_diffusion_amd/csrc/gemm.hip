@@ -1,6 +1,7 @@
-// LM-head product for many hidden rows (M > 128), where it is bound by the matrix cores rather
-// than by streaming W ("Nemotron-Labs-TwoTower" wiki page, section "Block-wise generation": every
-// denoising step predicts all masked positions of every block in parallel).
+// LM-head product for many hidden rows (M > 64) ("Nemotron-Labs-TwoTower" wiki page, section
+// "Block-wise generation": every denoising step predicts all masked positions of every block in
+// parallel). At these sizes re-reading the hidden rows from L2 and the matrix cores, rather than
+// streaming W, set the pace.
 //
 // Built with the iterative ILP machine scheduler (see build.py): with one wave per SIMD the
 // kernel relies on the next k-step's LDS reads being in flight while the current MFMAs run,
@@ -151,18 +152,23 @@ __global__ __launch_bounds__(LM_THREADS, 1) __attribute__((amdgpu_waves_per_eu(1
     }
 }
 
-}  // namespace
 
-#ifndef TT_GEMM_WM
-#define TT_GEMM_WM 2
-#endif
-
-int tt_lm_gemm_launch(const void* hidden, const void* w, float* logits, int M, int H, int V, hipStream_t s) {
-  constexpr int WM = TT_GEMM_WM, BM = 128 * WM, BN = 128 * (LM_WAVES / WM);
+template <int WM>
+int gemm_launch(const void* hidden, const void* w, float* logits, int M, int H, int V, hipStream_t s) {
+  constexpr int BM = 128 * WM, BN = 128 * (LM_WAVES / WM);
   const int nvt = (V + BN - 1) / BN;
   const int nmb = (M + BM - 1) / BM;
   const unsigned grid = (unsigned)(((nvt + NXCD - 1) / NXCD) * NXCD * nmb);
   hipLaunchKernelGGL(lmhead_gemm_kernel<WM>, dim3(grid), dim3(LM_THREADS), 0, s, (const bf16*)hidden,
                      (const bf16*)w, logits, M, H, V, nvt, nmb);
   return tt_launch_status();
+}
+
+}  // namespace
+
+// Tile by M (measured at H = 2688, V = 131072): up to 128 hidden rows, 128 x 512 tiles (W read
+// once, few re-reads of the hidden rows); beyond, 256 x 256 (two hidden-row blocks share W in L2).
+int tt_lm_gemm_launch(const void* hidden, const void* w, float* logits, int M, int H, int V, hipStream_t s) {
+  if (M <= 128) return gemm_launch<1>(hidden, w, logits, M, H, V, s);
+  return gemm_launch<2>(hidden, w, logits, M, H, V, s);
 }

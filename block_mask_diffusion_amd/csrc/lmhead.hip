@@ -393,14 +393,15 @@ int lm_lds_launch(const void* hidden, const void* w, float* logits, int M, int H
   return tt_launch_status();
 }
 
-// Tile configurations (measured on MI355X at H = 2688, V = 131072):
-//   LDS-staged <MT, BMT, VT, KW, NT, NSET> per hidden-row bucket;
-//   direct <MT, BMT, VT, STEP, RING, KCH> for larger M, fp32, or H not a multiple of KW.
+// Kernel choice (measured on MI355X at H = 2688, V = 131072): M <= 64 the LDS-staged kernel
+// <MT, BMT, VT, KW, NT, NSET> per hidden-row bucket; M > 64 the MFMA GEMM kernel (gemm.hip);
+// the direct kernel <MT, BMT, VT, STEP, RING, KCH> for fp32 and for H not a multiple of the
+// stage width.
 #ifndef TT_LM_LDS16
-#define TT_LM_LDS16 16, 1, 2, 128, true, 4
+#define TT_LM_LDS16 16, 1, 4, 64, true, 4
 #endif
 #ifndef TT_LM_LDS64
-#define TT_LM_LDS64 16, 4, 1, 128, true, 4
+#define TT_LM_LDS64 16, 4, 2, 64, true, 4
 #endif
 #ifndef TT_LM_LDS128
 #define TT_LM_LDS128 32, 4, 1, 64, true, 4
@@ -428,13 +429,17 @@ int lm_direct(const void* h, const void* w, float* o, int M, int H, int V, hipSt
   return lm_launch<bf16, MT, BMT, VT, STEP, RING, KCH>(h, w, o, M, H, V, s);
 }
 
+#ifndef TT_GEMM_MIN_M
+#define TT_GEMM_MIN_M 65
+#endif
+
 int lm_bf16(const void* h, const void* w, float* o, int M, int H, int V, hipStream_t s) {
+  if (M >= TT_GEMM_MIN_M && H % TT_GEMM_KB == 0) return tt_lm_gemm_launch(h, w, o, M, H, V, s);
   int st = 1;
   if (M <= 16) st = lm_try_lds<TT_LM_LDS16>(h, w, o, M, H, V, s);
   else if (M <= 64) st = lm_try_lds<TT_LM_LDS64>(h, w, o, M, H, V, s);
   else if (M <= 128) st = lm_try_lds<TT_LM_LDS128>(h, w, o, M, H, V, s);
   if (st != 1) return st;
-  if (M > 128 && H % TT_GEMM_KB == 0) return tt_lm_gemm_launch(h, w, o, M, H, V, s);
   if (M <= 32) return lm_direct<TT_LM_CFG32>(h, w, o, M, H, V, s);
   if (M <= 64) return lm_direct<TT_LM_CFG64>(h, w, o, M, H, V, s);
   return lm_direct<TT_LM_CFGBIG>(h, w, o, M, H, V, s);
