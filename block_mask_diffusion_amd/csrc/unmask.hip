@@ -15,7 +15,10 @@
 namespace {
 
 constexpr int UM_THREADS = 256;
-constexpr int UM_PER_THREAD = 16;
+#ifndef TT_UM_PER_THREAD
+#define TT_UM_PER_THREAD 16
+#endif
+constexpr int UM_PER_THREAD = TT_UM_PER_THREAD;
 constexpr int UM_CHUNK = UM_THREADS * UM_PER_THREAD;  // vocabulary entries per workgroup
 constexpr float LOG2E = 1.4426950408889634f;
 
