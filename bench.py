@@ -215,6 +215,31 @@ def main():
         if ev is not None:
             ev[4].record(stream)
 
+    # the fused leg: the same step with tt_lmhead_unmask in place of LM head + spikes + unmask
+    # (the spikes enter as its one-entry-per-row logit bias; the logits are never stored)
+    spk_tok_d = torch.from_numpy(sp["tok"].astype(np.int32)).to(dev)
+    ws_fu = torch.empty(max(256, bmd.workspace_bytes("tt_lmhead_unmask", B=wl.B, S=wl.S, H=wl.H, V=wl.V)),
+                        dtype=torch.uint8, device=dev)
+    nm_hist_fu = torch.zeros((K, wl.B), dtype=torch.int32, device=dev)
+
+    def step_fused(t, nm_out, ev=None):
+        s = t % wl.T
+        if s == 0:
+            tokens_d.copy_(tok0_d)
+            bits_d.copy_(bits0_d)
+        if ev is not None:
+            ev[0].record(stream)
+        for a, o in zip(attn_d, attn_out):
+            bmd.tt_block_attn(a["q"], a["k_blk"], a["v_blk"], a["k_ctx"], a["v_ctx"], a["ctx_start"],
+                              a["ctx_len"], max_prefix=wl.max_prefix, softmax_scale=a["scale"], out=o,
+                              workspace=ws_attn)
+        if ev is not None:
+            ev[1].record(stream)
+        bmd.tt_lmhead_unmask(hidden_d, w_d, tokens_d, bits_d, nm_out, s, wl.T, wl.gamma, wl.mask_id,
+                             bias_tok=spk_tok_d, bias_val=spk_val_d, workspace=ws_fu)
+        if ev is not None:
+            ev[2].record(stream)
+
     for t in range(Wm):
         step(t, nm_scratch)
     torch.cuda.synchronize()
@@ -231,21 +256,41 @@ def main():
     wall = time.perf_counter() - t_wall
     total_ms = start.elapsed_time(end)
 
+    # fused leg, timed the same way after its own warmup
+    for t in range(Wm):
+        step_fused(t, nm_scratch)
+    evs_fu = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    start_fu, end_fu = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start_fu.record(stream)
+    for t in range(K):
+        step_fused(t, nm_hist_fu[t], evs_fu[t])
+    end_fu.record(stream)
+    torch.cuda.synchronize()
+    total_ms_fu = start_fu.elapsed_time(end_fu)
+    t_fu = sum(e[1].elapsed_time(e[2]) for e in evs_fu) / K
+
     t_attn = sum(e[0].elapsed_time(e[1]) for e in evs) / K
     t_lm = sum(e[1].elapsed_time(e[2]) for e in evs) / K
     t_spk = sum(e[2].elapsed_time(e[3]) for e in evs) / K
     t_um = sum(e[3].elapsed_time(e[4]) for e in evs) / K
 
     # block-steps and commits from the per-step n_masked record
-    nm = nm_hist.cpu().numpy()
     init_masked = np.array([bin(int(b)).count("1") for b in st0["mask_bits"]])
-    block_steps, commits, masked_rows = 0, 0, 0
-    for t in range(K):
-        start_masked = init_masked if t % wl.T == 0 else nm[t - 1]
-        block_steps += int(np.sum(start_masked > 0))
-        commits += int(np.sum(start_masked - nm[t]))
-        masked_rows += int(np.sum(start_masked))
+
+    def tally(nm):
+        block_steps, commits, masked_rows = 0, 0, 0
+        for t in range(K):
+            start_masked = init_masked if t % wl.T == 0 else nm[t - 1]
+            block_steps += int(np.sum(start_masked > 0))
+            commits += int(np.sum(start_masked - nm[t]))
+            masked_rows += int(np.sum(start_masked))
+        return block_steps, commits, masked_rows
+
+    block_steps, commits, masked_rows = tally(nm_hist.cpu().numpy())
+    block_steps_fu, commits_fu, _ = tally(nm_hist_fu.cpu().numpy())
     sec = total_ms / 1e3
+    sec_fu = total_ms_fu / 1e3
     alg = algorithmic(wl)
     lm_gbs = alg["lm_bytes"] / (t_lm / 1e3) / 1e9
     t_attn_call = t_attn / wl.layers  # ms per tt_block_attn call (one layer)
@@ -315,6 +360,16 @@ def main():
                        "attainable_frac": round(lm_tfs / lm_attain_tfs, 4)},
             "unmask": {"us": round(t_um * 1e3, 2), "GB_s": round(um_gbs, 1), "hbm_frac": round(um_gbs / HBM_PEAK_GBS, 4)},
             "spikes_us": round(t_spk * 1e3, 2),
+        },
+        "fused_path": {
+            "what": "same step with tt_lmhead_unmask (LM head with the vocabulary reduction in its epilogue, "
+                    "spikes as its logit bias, logits never stored) in place of LM head + spikes + unmask",
+            "block_steps_per_s": round(block_steps_fu / sec_fu, 2),
+            "committed_tokens_per_s": round(commits_fu / sec_fu, 2),
+            "ms_per_step": round(total_ms_fu / K, 4),
+            "lmhead_unmask_us": round(t_fu * 1e3, 2),
+            "lmhead_unmask_hbm_frac": round((alg["lm_bytes"] - 4.0 * wl.M * wl.V) / (t_fu / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+            "lmhead_unmask_mfma_frac": round(alg["lm_flops"] / (t_fu / 1e3) / 1e12 / MFMA_BF16_PEAK_TFS, 4),
         },
         "wall_s_timed": round(wall, 3),
         "input_gen_s": round(gen_s, 1),

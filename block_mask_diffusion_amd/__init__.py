@@ -1,8 +1,8 @@
 """TwoTower denoiser block step on AMD CDNA4 (gfx950).
 
-Python face of libtt.so: the three calls of include/tt.h under the same names, taking torch
-tensors. This layer only marshals arguments (shapes, dtypes, pointers, the current HIP stream,
-workspace allocation); every step of the computation runs in the HIP kernels of the library.
+Python face of libtt.so: the calls of include/tt.h under the same names, taking torch tensors.
+This layer only marshals arguments (shapes, dtypes, pointers, the current HIP stream, workspace
+allocation); every step of the computation runs in the HIP kernels of the library.
 """
 from __future__ import annotations
 
@@ -15,8 +15,8 @@ import torch
 from . import _lib
 from ._lib import TTError, TT_BF16, TT_F32
 
-__all__ = ["tt_block_attn", "tt_lmhead_logits", "tt_confidence_unmask", "workspace_bytes",
-           "TTError", "abi_version"]
+__all__ = ["tt_block_attn", "tt_lmhead_logits", "tt_confidence_unmask", "tt_lmhead_unmask",
+           "workspace_bytes", "TTError", "abi_version"]
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -57,8 +57,8 @@ def abi_version() -> int:
 
 
 def workspace_bytes(fn: str, **kw) -> int:
-    """Workspace size of `tt_block_attn` / `tt_confidence_unmask` for the given sizes
-    (a pure host computation: nothing is launched)."""
+    """Workspace size of `tt_block_attn` / `tt_confidence_unmask` / `tt_lmhead_unmask` for the
+    given sizes (a pure host computation: nothing is launched)."""
     lib = _lib.load()
     n = ctypes.c_size_t(0)
     if fn == "tt_block_attn":
@@ -71,6 +71,11 @@ def workspace_bytes(fn: str, **kw) -> int:
         one = ctypes.c_void_p(16)
         st = lib.tt_confidence_unmask(one, one, one, one, None, None, kw["B"], kw["S"], kw["V"], 0, 1,
                                       0.5, kw.get("mask_id", 0), None, ctypes.byref(n), None)
+    elif fn == "tt_lmhead_unmask":
+        one = ctypes.c_void_p(16)
+        st = lib.tt_lmhead_unmask(one, one, None, None, one, one, one, None, None, kw["B"], kw["S"], kw["H"],
+                                  kw["V"], 0, 1, 0.5, kw.get("mask_id", 0), kw.get("dtype", TT_BF16), None,
+                                  ctypes.byref(n), None)
     else:
         raise ValueError(fn)
     _check(st, fn)
@@ -146,12 +151,7 @@ def tt_confidence_unmask(logits: torch.Tensor, tokens: torch.Tensor, mask_bits: 
     B, S = tokens.shape
     _need(logits.dtype == torch.float32 and logits.dim() == 2 and logits.shape[0] == B * S, "logits fp32 [B*S][V]")
     V = logits.shape[1]
-    _need(mask_bits.dtype in (torch.int64, torch.uint64) and mask_bits.numel() == B, "mask_bits 64-bit [B]")
-    _need(n_masked.dtype == torch.int32 and n_masked.numel() == B, "n_masked int32 [B]")
-    if conf_out is not None:
-        _need(conf_out.dtype == torch.float32 and conf_out.numel() == B * S, "conf_out fp32 [B*S]")
-    if pred_out is not None:
-        _need(pred_out.dtype == torch.int32 and pred_out.numel() == B * S, "pred_out int32 [B*S]")
+    _unmask_io(B, S, tokens, mask_bits, n_masked, conf_out, pred_out)
     _dev(logits, tokens, mask_bits, n_masked, conf_out, pred_out)
     lib = _lib.load()
     n = ctypes.c_size_t(0)
@@ -161,3 +161,44 @@ def tt_confidence_unmask(logits: torch.Tensor, tokens: torch.Tensor, mask_bits: 
     ws = _workspace(n.value, workspace, logits.device)
     n2 = ctypes.c_size_t(ws.numel() * ws.element_size())
     _check(lib.tt_confidence_unmask(*args, _ptr(ws), ctypes.byref(n2), _stream(stream)), "tt_confidence_unmask")
+
+
+def _unmask_io(B: int, S: int, tokens, mask_bits, n_masked, conf_out, pred_out):
+    _need(mask_bits.dtype in (torch.int64, torch.uint64) and mask_bits.numel() == B, "mask_bits 64-bit [B]")
+    _need(n_masked.dtype == torch.int32 and n_masked.numel() == B, "n_masked int32 [B]")
+    if conf_out is not None:
+        _need(conf_out.dtype == torch.float32 and conf_out.numel() == B * S, "conf_out fp32 [B*S]")
+    if pred_out is not None:
+        _need(pred_out.dtype == torch.int32 and pred_out.numel() == B * S, "pred_out int32 [B*S]")
+
+
+def tt_lmhead_unmask(hidden: torch.Tensor, w: torch.Tensor, tokens: torch.Tensor, mask_bits: torch.Tensor,
+                     n_masked: torch.Tensor, step: int, num_steps: int, gamma: float, mask_id: int,
+                     bias_tok: Optional[torch.Tensor] = None, bias_val: Optional[torch.Tensor] = None,
+                     conf_out: Optional[torch.Tensor] = None, pred_out: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """LM head + one confidence-unmasking step without materialising the logits (see
+    include/tt.h). hidden bf16 [B*S][H], w bf16 [V][H]; tokens int32 [B][S] and mask_bits
+    (64-bit) [B] are updated in place; optional one-entry-per-row logit bias bias_tok int32 /
+    bias_val fp32 [B*S]."""
+    _need(tokens.dim() == 2 and tokens.dtype == torch.int32, "tokens int32 [B][S]")
+    B, S = tokens.shape
+    _need(hidden.dim() == 2 and w.dim() == 2 and hidden.shape[1] == w.shape[1], "hidden [M][H], w [V][H]")
+    _need(hidden.shape[0] == B * S, "hidden has B*S rows")
+    _need(hidden.dtype == w.dtype, "hidden and w share one dtype")
+    _need((bias_tok is None) == (bias_val is None), "bias_tok and bias_val go together")
+    if bias_tok is not None:
+        _need(bias_tok.dtype == torch.int32 and bias_tok.numel() == B * S, "bias_tok int32 [B*S]")
+        _need(bias_val.dtype == torch.float32 and bias_val.numel() == B * S, "bias_val fp32 [B*S]")
+    _unmask_io(B, S, tokens, mask_bits, n_masked, conf_out, pred_out)
+    _dev(hidden, w, tokens, mask_bits, n_masked, bias_tok, bias_val, conf_out, pred_out)
+    H, V = hidden.shape[1], w.shape[0]
+    lib = _lib.load()
+    n = ctypes.c_size_t(0)
+    args = [_ptr(hidden), _ptr(w), _ptr(bias_tok), _ptr(bias_val), _ptr(tokens), _ptr(mask_bits), _ptr(n_masked),
+            _ptr(conf_out), _ptr(pred_out), B, S, H, V, int(step), int(num_steps), float(gamma), int(mask_id),
+            _dtype(hidden)]
+    _check(lib.tt_lmhead_unmask(*args, None, ctypes.byref(n), None), "tt_lmhead_unmask")
+    ws = _workspace(n.value, workspace, hidden.device)
+    n2 = ctypes.c_size_t(ws.numel() * ws.element_size())
+    _check(lib.tt_lmhead_unmask(*args, _ptr(ws), ctypes.byref(n2), _stream(stream)), "tt_lmhead_unmask")

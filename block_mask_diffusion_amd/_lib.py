@@ -21,8 +21,8 @@ TT_F32, TT_BF16 = 0, 1
 TT_OK, TT_ERR_ARG, TT_ERR_UNSUPPORTED, TT_ERR_WORKSPACE, TT_ERR_HIP = 0, -1, -2, -3, -4
 
 # every symbol include/tt.h declares
-EXPORTS = ("tt_block_attn", "tt_lmhead_logits", "tt_confidence_unmask", "tt_status_string",
-           "tt_abi_version")
+EXPORTS = ("tt_block_attn", "tt_lmhead_logits", "tt_confidence_unmask", "tt_lmhead_unmask",
+           "tt_status_string", "tt_abi_version")
 
 _lib = None
 
@@ -62,6 +62,8 @@ def load() -> ctypes.CDLL:
     lib.tt_lmhead_logits.restype = i
     lib.tt_confidence_unmask.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f32, i, vp, sz, vp]
     lib.tt_confidence_unmask.restype = i
+    lib.tt_lmhead_unmask.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f32, i, i, vp, sz, vp]
+    lib.tt_lmhead_unmask.restype = i
     lib.tt_status_string.argtypes = [i]
     lib.tt_status_string.restype = ctypes.c_char_p
     lib.tt_abi_version.argtypes = []

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "tt.h"
 
 typedef __bf16 bf16;
@@ -49,6 +51,20 @@ __device__ __forceinline__ float tt_swap_halves(float v) {
   const unsigned u = __float_as_uint(v);
   const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
   return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
+__device__ __forceinline__ int tt_swap_halves_i(int v) {
+  const auto r = __builtin_amdgcn_permlane32_swap((unsigned)v, (unsigned)v, false, false);
+  return (int)((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
+// f(std::integral_constant<int, i>) for i = 0 .. N-1 (a compile-time index for each call)
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void tt_static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    tt_static_for<N, I + 1>(f);
+  }
 }
 
 // exp2 on the hardware transcendental unit (v_exp_f32): exact at 0, returns 0 for -inf.
@@ -96,4 +112,21 @@ __device__ __forceinline__ void tt_dma16(const void* gptr, uint32_t lds_base) {
       : "=&s"(saved)
       : "v"(gptr), "s"(lds_base)
       : "memory");
+}
+
+// The same with the LDS address given as a base plus a constant byte offset, added into M0 inside
+// the asm: a loop that fills many slots from one base keeps a single scalar register live.
+template <int OFF>
+__device__ __forceinline__ void tt_dma16_at(const void* gptr, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_add_u32 m0, %2, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_nop 0\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(gptr), "s"(lds_base), "i"(OFF)
+      : "memory", "scc");
 }

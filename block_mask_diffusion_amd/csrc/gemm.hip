@@ -7,6 +7,9 @@
 // kernel relies on the next k-step's LDS reads being in flight while the current MFMAs run,
 // which the default occupancy-oriented schedule undoes by sinking each read next to its use.
 #include "lmhead_int.h"
+#include "reduce_int.h"
+
+#include <type_traits>
 
 namespace {
 
@@ -38,10 +41,13 @@ __device__ __forceinline__ int gm_swz(int r) { return (r >> 1) & 7; }
 
 // WM waves along the hidden rows, 4 / WM along the vocabulary, each owning a 128 x 128 block:
 // tile BM = 128 WM hidden rows x BN = 128 (4 / WM) vocabulary rows.
-template <int WM>
+// RED = false: store the fp32 logits. RED = true: reduce each row's logits over the wave's 128
+// columns to one (max, lowest argmax, sum exp) record in red.parts[row][vtile * WN + wn]; the
+// logits never reach memory.
+template <int WM, bool RED>
 __global__ __launch_bounds__(LM_THREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void lmhead_gemm_kernel(
     const bf16* __restrict__ hidden, const bf16* __restrict__ w, float* __restrict__ logits, int M, int H,
-    int V, int nvt, int nmb) {
+    int V, int nvt, int nmb, TtRedArgs red) {
   constexpr int WN = LM_WAVES / WM;
   constexpr int GM_BM = 128 * WM, GM_BN = 128 * WN;
   constexpr int ASTAGE = GM_BM * GM_ROWB, BSTAGE = GM_BN * GM_ROWB;  // bytes per stage
@@ -78,12 +84,14 @@ __global__ __launch_bounds__(LM_THREADS, 1) __attribute__((amdgpu_waves_per_eu(1
     const int r = (wave * BCPW + i) * 8 + lane / 8;
     bsrc[i] = w + (size_t)min(v0 + r, V - 1) * H + 8 * ((lane & 7) ^ gm_swz(r));
   }
+  // this wave's first LDS slot of stage buffer 0 in each ring; the rest are constant offsets
+  const uint32_t a_lds = tt_lds_addr(&sa[0][wave * ACPW * 1024]);
+  const uint32_t b_lds = tt_lds_addr(&sb[0][wave * BCPW * 1024]);
   auto issue = [&](int st) {
     const int buf = st % GM_NBUF, k0 = st * GM_KB;
-#pragma unroll
-    for (int i = 0; i < ACPW; ++i) tt_dma16(asrc[i] + k0, tt_lds_addr(&sa[buf][(wave * ACPW + i) * 1024]));
-#pragma unroll
-    for (int i = 0; i < BCPW; ++i) tt_dma16(bsrc[i] + k0, tt_lds_addr(&sb[buf][(wave * BCPW + i) * 1024]));
+    const uint32_t ab = a_lds + buf * ASTAGE, bb = b_lds + buf * BSTAGE;
+    tt_static_for<ACPW>([&](auto i) { tt_dma16_at<i * 1024>(asrc[i] + k0, ab); });
+    tt_static_for<BCPW>([&](auto i) { tt_dma16_at<i * 1024>(bsrc[i] + k0, bb); });
   };
 
   f32x16 acc[4][4];
@@ -111,12 +119,10 @@ __global__ __launch_bounds__(LM_THREADS, 1) __attribute__((amdgpu_waves_per_eu(1
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
-        acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mt], fb[nt], acc[mt][nt], 0, 0, 0);
+        acc[mt][nt] = RED ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[nt], fa[mt], acc[mt][nt], 0, 0, 0)
+                          : __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mt], fb[nt], acc[mt][nt], 0, 0, 0);
   };
 
-  // Stage st: wait for this wave's loads of it (the only ones outstanding), barrier (every
-  // wave's loads are in LDS and stage st - 1 has been read by all), refill the other buffer with
-  // stage st + 1, then 4 k-steps with the fragments of step ks + 1 read during step ks.
   // Stage st: wait for this wave's loads of it (the only ones outstanding), barrier (every
   // wave's loads are in LDS and stage st - 1 has been read by all), refill the other buffer with
   // stage st + 1, then GM_KS k-steps with the fragments of step ks + 1 read during step ks.
@@ -138,29 +144,137 @@ __global__ __launch_bounds__(LM_THREADS, 1) __attribute__((amdgpu_waves_per_eu(1
     }
   }
 
+  if constexpr (RED) {
+    // The fused path multiplies W by the hidden rows (operands swapped), so each accumulator
+    // tile holds logits transposed: lane l, register j of tile (mt, nt) is hidden row
+    // 32 mt + l % 32 and vocabulary id cb + 32 nt + 8 (j / 4) + 4 (l / 32) + j % 4. A lane thus
+    // holds 64 of its row's 128 logits and lane l ^ 32 the other 64: the row reduction runs in
+    // registers, with one exchange between the two halves of the wave.
+    const int cb = v0 + 128 * wn;  // first vocabulary id of the block
+    if (cb >= V) return;
+    const int part = vtile * WN + wn;
+    // only blocks that hold the mask id, the vocabulary's end or some row's bias entry (a wave-
+    // uniform test) pay for the per-entry checks
+    const bool special = (red.mask_id >= cb && red.mask_id < cb + 128) || (cb + 128 > V);
+    int btok[4];
+    float bval[4];
+    bool hit = false;
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int v = v0 + 128 * wn + 32 * nt + l32;
-      if (v >= V) continue;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int m = m0 + 128 * wm + 32 * mt + mrow(lane, j);
-        if (m < M) logits[(size_t)m * V + v] = acc[mt][nt][j];
-      }
+    for (int mt = 0; mt < 4; ++mt) {
+      const int mc = min(m0 + 128 * wm + 32 * mt + l32, M - 1);
+      btok[mt] = red.bias_tok ? red.bias_tok[mc] : -1;
+      bval[mt] = red.bias_tok ? red.bias_val[mc] : 0.f;
+      hit = hit || (btok[mt] >= cb && btok[mt] < cb + 128);
     }
+    // vocabulary id of v[k] below: increasing in k for a fixed lane
+    auto vid = [&](int k) { return cb + 32 * (k >> 4) + 8 * ((k & 15) >> 2) + 4 * hh + (k & 3); };
+    // three instances, so that the wave-uniform choice stays a branch: plain; one row's bias
+    // entry may lie in the block (about one block in eight at 512 rows); mask id or vocabulary
+    // end in the block (every check, rare)
+    auto reduce_rows = [&](auto mode) {
+      constexpr int MODE = decltype(mode)::value;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        float v[64];
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) v[16 * nt + j] = acc[mt][nt][j];
+        if constexpr (MODE == 1) {
+          // v[k] gets the bias where vid(k) == btok; compares kept in small groups (hoisted, their
+          // masks overflow the scalar registers)
+          const int rel = btok[mt] - vid(0);
+#pragma unroll
+          for (int k = 0; k < 64; ++k) {
+            v[k] = (rel == vid(k) - vid(0)) ? v[k] + bval[mt] : v[k];
+            if ((k & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+          }
+        } else if constexpr (MODE == 2) {
+          // as above, then the mask id and ids past the vocabulary's end become -inf
+          const int rel = btok[mt] - vid(0), relm = red.mask_id - vid(0), relv = V - vid(0);
+#pragma unroll
+          for (int k = 0; k < 64; ++k) {
+            const int d = vid(k) - vid(0);
+            const float x = (rel == d) ? v[k] + bval[mt] : v[k];
+            v[k] = (relm == d || d >= relv) ? -INFINITY : x;
+            if ((k & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        float mx[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          mx[q] = v[8 * q];
+#pragma unroll
+          for (int e = 1; e < 8; ++e) mx[q] = fmaxf(mx[q], v[8 * q + e]);
+        }
+#pragma unroll
+        for (int w2 = 4; w2 >= 1; w2 >>= 1)
+#pragma unroll
+          for (int q = 0; q < w2; ++q) mx[q] = fmaxf(mx[q], mx[q + w2]);
+        const float rm = fmaxf(mx[0], tt_swap_halves(mx[0]));
+        const bool empty = (rm == -INFINITY);
+        const float mb = empty ? 0.f : rm * TT_LOG2E;
+        int kf = 64;  // first k (lowest id) of this lane holding the maximum; 64 = none
+#pragma unroll
+        for (int k = 63; k >= 0; --k) {
+          kf = (v[k] == rm) ? k : kf;
+          // keeps the compares next to their selects: hoisted, their masks overflow the SGPRs
+          if ((k & 7) == 0) __builtin_amdgcn_sched_barrier(0);
+        }
+        int key = (kf < 64) ? vid(kf) : INT32_MAX;
+        float sm[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          sm[q] = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sm[q] += tt_exp2(fmaf(v[8 * q + e], TT_LOG2E, -mb));
+        }
+#pragma unroll
+        for (int w2 = 4; w2 >= 1; w2 >>= 1)
+#pragma unroll
+          for (int q = 0; q < w2; ++q) sm[q] += sm[q + w2];
+        const float rs = sm[0] + tt_swap_halves(sm[0]);  // same sum on both halves (commutative)
+        key = min(key, tt_swap_halves_i(key));
+        const int m = m0 + 128 * wm + 32 * mt + l32;
+        if (hh == 0 && m < M) {
+          TtPartial p;
+          p.m = rm;
+          p.s = rs;
+          p.a = empty ? INT32_MAX : key;
+          p.pad = 0;
+          red.parts[(size_t)m * red.nparts + part] = p;
+        }
+      }
+    };
+    if (special) reduce_rows(std::integral_constant<int, 2>{});
+    else if (__any(hit)) reduce_rows(std::integral_constant<int, 1>{});
+    else reduce_rows(std::integral_constant<int, 0>{});
+  } else {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int v = v0 + 128 * wn + 32 * nt + l32;
+        if (v >= V) continue;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int m = m0 + 128 * wm + 32 * mt + mrow(lane, j);
+          if (m < M) logits[(size_t)m * V + v] = acc[mt][nt][j];
+        }
+      }
+  }
 }
 
 
-template <int WM>
-int gemm_launch(const void* hidden, const void* w, float* logits, int M, int H, int V, hipStream_t s) {
+template <int WM, bool RED>
+int gemm_launch(const void* hidden, const void* w, float* logits, int M, int H, int V, TtRedArgs red,
+                hipStream_t s) {
   constexpr int BM = 128 * WM, BN = 128 * (LM_WAVES / WM);
   const int nvt = (V + BN - 1) / BN;
   const int nmb = (M + BM - 1) / BM;
   const unsigned grid = (unsigned)(((nvt + NXCD - 1) / NXCD) * NXCD * nmb);
-  hipLaunchKernelGGL(lmhead_gemm_kernel<WM>, dim3(grid), dim3(LM_THREADS), 0, s, (const bf16*)hidden,
-                     (const bf16*)w, logits, M, H, V, nvt, nmb);
+  hipLaunchKernelGGL((lmhead_gemm_kernel<WM, RED>), dim3(grid), dim3(LM_THREADS), 0, s, (const bf16*)hidden,
+                     (const bf16*)w, logits, M, H, V, nvt, nmb, red);
   return tt_launch_status();
 }
 
@@ -169,6 +283,15 @@ int gemm_launch(const void* hidden, const void* w, float* logits, int M, int H, 
 // Tile by M (measured at H = 2688, V = 131072): up to 128 hidden rows, 128 x 512 tiles (W read
 // once, few re-reads of the hidden rows); beyond, 256 x 256 (two hidden-row blocks share W in L2).
 int tt_lm_gemm_launch(const void* hidden, const void* w, float* logits, int M, int H, int V, hipStream_t s) {
-  if (M <= 128) return gemm_launch<1>(hidden, w, logits, M, H, V, s);
-  return gemm_launch<2>(hidden, w, logits, M, H, V, s);
+  const TtRedArgs none{nullptr, nullptr, -1, nullptr, 0};
+  if (M <= 128) return gemm_launch<1, false>(hidden, w, logits, M, H, V, none, s);
+  return gemm_launch<2, false>(hidden, w, logits, M, H, V, none, s);
+}
+
+// Fused variant: per-(row, 128-column block) reduction records instead of logits; red.nparts
+// must be ceil(V / 128).
+int tt_lm_gemm_reduce_launch(const void* hidden, const void* w, int M, int H, int V, TtRedArgs red,
+                             hipStream_t s) {
+  if (M <= 128) return gemm_launch<1, true>(hidden, w, nullptr, M, H, V, red, s);
+  return gemm_launch<2, true>(hidden, w, nullptr, M, H, V, red, s);
 }

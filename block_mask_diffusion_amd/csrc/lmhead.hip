@@ -20,6 +20,7 @@
 // When M needs several hidden-row blocks, the workgroups of one vocabulary tile are placed on the
 // same XCD (dispatch ids congruent modulo 8 land on the same XCD), so the blocks share W in L2.
 #include "lmhead_int.h"
+#include "reduce_int.h"
 
 namespace {
 
@@ -249,11 +250,13 @@ int lm_launch(const void* hidden, const void* w, float* logits, int M, int H, in
 // each stage covers KW columns of h for the TV vocabulary rows and the MB hidden rows of the
 // workgroup. NSET register sets keep up to NSET stages of global loads in flight; LDS is double
 // buffered, so one barrier per stage separates the writes of stage g+1 from the reads of stage g.
-template <int MT, int BMT, int VT, int KW, bool NT, int NSET>
+// RED = true: instead of storing logits, reduce each row over the wave's VT * NV columns to one
+// (max, lowest argmax, sum exp) record in red.parts[row][vtile * LM_WAVES + wave].
+template <int MT, int BMT, int VT, int KW, bool NT, int NSET, bool RED = false>
 __global__ __launch_bounds__(LM_THREADS) void lmhead_lds_kernel(const bf16* __restrict__ hidden,
                                                                const bf16* __restrict__ w,
                                                                float* __restrict__ logits, int M, int H,
-                                                               int V, int nvt, int nmb) {
+                                                               int V, int nvt, int nmb, TtRedArgs red) {
   typedef Shape<bf16, MT> SH;
   typedef typename SH::frag frag;
   typedef typename SH::acc acc_t;
@@ -366,32 +369,102 @@ __global__ __launch_bounds__(LM_THREADS) void lmhead_lds_kernel(const bf16* __re
     }
   }
 
+  if constexpr (RED) {
+    // the NV lanes of a group share NREG rows per hidden tile; reduce over their VT * NV columns
+    constexpr int W = VT * NV;
+    const int cb = v0 + wave * W;
+    if (cb >= V) return;
+    const int part = vtile * LM_WAVES + wave;
+    // wave-uniform choice: only blocks holding the mask id, the vocabulary's end or some row's
+    // bias entry need the per-entry checks
+    bool slow = (red.mask_id >= cb && red.mask_id < cb + W) || (cb + W > V);
+    if (red.bias_tok) {
+      bool hit = false;
 #pragma unroll
-  for (int mt = 0; mt < BMT; ++mt)
-#pragma unroll
-    for (int vt = 0; vt < VT; ++vt) {
-      const int v = v0 + (wave * VT + vt) * NV + col;
-      if (v >= V) continue;
-#pragma unroll
-      for (int j = 0; j < NREG; ++j) {
-        const int m = m0 + mt * MT + SH::row(lane, j);
-        if (m < M) logits[(size_t)m * V + v] = acc[mt][vt][j];
+      for (int r = lane; r < MB; r += 64) {
+        const int m = m0 + r;
+        if (m < M) {
+          const int t = red.bias_tok[m];
+          hit = hit || (t >= cb && t < cb + W);
+        }
       }
+      slow = slow || __any(hit);
     }
+    auto emit = [&](int m, float rm, int ra, float rs) {
+      if (col == 0 && m < M) {
+        TtPartial p;
+        p.m = rm;
+        p.s = rs;
+        p.a = ra;
+        p.pad = 0;
+        red.parts[(size_t)m * red.nparts + part] = p;
+      }
+    };
+    if (!slow) {
+#pragma unroll
+      for (int mt = 0; mt < BMT; ++mt)
+#pragma unroll
+        for (int j = 0; j < NREG; ++j) {
+          float v[VT];
+#pragma unroll
+          for (int vt = 0; vt < VT; ++vt) v[vt] = acc[mt][vt][j];
+          float rm, rs;
+          int ra;
+          tt_row_reduce<VT, NV>(v, cb, NV, col, rm, ra, rs);
+          emit(m0 + mt * MT + SH::row(lane, j), rm, ra, rs);
+        }
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < BMT; ++mt)
+#pragma unroll
+        for (int j = 0; j < NREG; ++j) {
+          const int m = m0 + mt * MT + SH::row(lane, j);
+          const int mc = min(m, M - 1);
+          const int btok = red.bias_tok ? red.bias_tok[mc] : -1;
+          const float bval = red.bias_tok ? red.bias_val[mc] : 0.f;
+          float v[VT];
+#pragma unroll
+          for (int vt = 0; vt < VT; ++vt)
+            v[vt] = tt_red_logit(acc[mt][vt][j], cb + vt * NV + col, V, btok, bval, red.mask_id);
+          float rm, rs;
+          int ra;
+          tt_row_reduce<VT, NV>(v, cb, NV, col, rm, ra, rs);
+          emit(m, rm, ra, rs);
+        }
+    }
+  } else {
+#pragma unroll
+    for (int mt = 0; mt < BMT; ++mt)
+#pragma unroll
+      for (int vt = 0; vt < VT; ++vt) {
+        const int v = v0 + (wave * VT + vt) * NV + col;
+        if (v >= V) continue;
+#pragma unroll
+        for (int j = 0; j < NREG; ++j) {
+          const int m = m0 + mt * MT + SH::row(lane, j);
+          if (m < M) logits[(size_t)m * V + v] = acc[mt][vt][j];
+        }
+      }
+  }
 }
 
-template <int MT, int BMT, int VT, int KW, bool NT, int NSET>
-int lm_lds_launch(const void* hidden, const void* w, float* logits, int M, int H, int V, hipStream_t s) {
+template <int MT, int BMT, int VT, int KW, bool NT, int NSET, bool RED = false>
+int lm_lds_launch(const void* hidden, const void* w, float* logits, int M, int H, int V, hipStream_t s,
+                  TtRedArgs red = TtRedArgs{nullptr, nullptr, -1, nullptr, 0}) {
   constexpr int TV = LM_WAVES * VT * Shape<bf16, MT>::NV;
   const int nvt = (V + TV - 1) / TV;
   const int nmb = (M + MT * BMT - 1) / (MT * BMT);
   unsigned grid;
   if (nmb == 1) grid = (unsigned)nvt;
   else grid = (unsigned)(((nvt + NXCD - 1) / NXCD) * NXCD * nmb);
-  hipLaunchKernelGGL((lmhead_lds_kernel<MT, BMT, VT, KW, NT, NSET>), dim3(grid), dim3(LM_THREADS), 0, s,
-                     (const bf16*)hidden, (const bf16*)w, logits, M, H, V, nvt, nmb);
+  hipLaunchKernelGGL((lmhead_lds_kernel<MT, BMT, VT, KW, NT, NSET, RED>), dim3(grid), dim3(LM_THREADS), 0, s,
+                     (const bf16*)hidden, (const bf16*)w, logits, M, H, V, nvt, nmb, red);
   return tt_launch_status();
 }
+
+// columns of one wave's reduction record in the fused path of an LDS-kernel configuration
+template <int MT, int BMT, int VT, int KW, bool NT, int NSET>
+constexpr int lds_cols_per_part() { return VT * Shape<bf16, MT>::NV; }
 
 // Kernel choice (measured on MI355X at H = 2688, V = 131072): M <= 64 the LDS-staged kernel
 // <MT, BMT, VT, KW, NT, NSET> per hidden-row bucket; M > 64 the MFMA GEMM kernel (gemm.hip);
@@ -446,6 +519,23 @@ int lm_bf16(const void* h, const void* w, float* o, int M, int H, int V, hipStre
 }
 
 }  // namespace
+
+// Fused LM head + vocabulary reduction (bf16, H % 64 == 0): which kernel, and how many records per
+// row it writes. M <= 16 and M <= 64 use the LDS-staged kernel of the same bucket as the logits
+// path, larger M the GEMM kernel (128 columns per record).
+int tt_lm_reduce_nparts(int M, int V) {
+  int cols;
+  if (M <= 16) cols = lds_cols_per_part<TT_LM_LDS16>();
+  else if (M <= 64) cols = lds_cols_per_part<TT_LM_LDS64>();
+  else cols = 128;
+  return (V + cols - 1) / cols;
+}
+
+int tt_lm_reduce_launch(const void* hidden, const void* w, int M, int H, int V, TtRedArgs red, hipStream_t s) {
+  if (M <= 16) return lm_lds_launch<TT_LM_LDS16, true>(hidden, w, nullptr, M, H, V, s, red);
+  if (M <= 64) return lm_lds_launch<TT_LM_LDS64, true>(hidden, w, nullptr, M, H, V, s, red);
+  return tt_lm_gemm_reduce_launch(hidden, w, M, H, V, red, s);
+}
 
 extern "C" int tt_lmhead_logits(const void* hidden, const void* w, float* logits, int M, int H,
                                 int V, int dtype, void* stream) {

@@ -10,3 +10,15 @@
 __attribute__((visibility("hidden"))) int tt_lm_gemm_launch(const void* hidden, const void* w,
                                                             float* logits, int M, int H, int V,
                                                             hipStream_t s);
+
+struct TtRedArgs;
+// Fused variant of the GEMM kernel: instead of logits, one (max, lowest argmax, sum exp) record
+// per (row, 128-column block) in red.parts (red.nparts = ceil(V / 128)).
+__attribute__((visibility("hidden"))) int tt_lm_gemm_reduce_launch(const void* hidden, const void* w,
+                                                                   int M, int H, int V, TtRedArgs red,
+                                                                   hipStream_t s);
+
+// Fused LM head + vocabulary reduction (bf16, H % TT_GEMM_KB == 0): records per row, and launch.
+__attribute__((visibility("hidden"))) int tt_lm_reduce_nparts(int M, int V);
+__attribute__((visibility("hidden"))) int tt_lm_reduce_launch(const void* hidden, const void* w, int M, int H,
+                                                              int V, TtRedArgs red, hipStream_t s);

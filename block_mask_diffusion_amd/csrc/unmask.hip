@@ -10,7 +10,12 @@
 //                   (deterministic) by four waves in parallel; lane i of wave 0 then holds
 //                   conf = 1 / sum and the prediction and applies the threshold, the completion
 //                   floor and the in-place token / bitmap update.
-#include "common.h"
+//
+// The fused LM head + unmask call (tt_lmhead_unmask) replaces the logits and unmask_partial with
+// the LM-head kernels' reduction epilogue (one record per row and column block of one wave),
+// merges each masked row's records with unmask_rowmerge and ends with the same unmask_commit.
+#include "lmhead_int.h"
+#include "reduce_int.h"
 
 namespace {
 
@@ -20,25 +25,41 @@ constexpr int UM_THREADS = 256;
 #endif
 constexpr int UM_PER_THREAD = TT_UM_PER_THREAD;
 constexpr int UM_CHUNK = UM_THREADS * UM_PER_THREAD;  // vocabulary entries per workgroup
-constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LOG2E = TT_LOG2E;
+typedef TtPartial Partial;
 
-struct alignas(16) Partial {
-  float m;  // chunk max (-inf when the chunk holds no eligible entry)
-  float s;  // sum of exp(l - m) over the chunk
-  int a;    // lowest index attaining m (INT32_MAX when none)
-  int pad;
-};
-
-// Merge two (max, argmax, sum) triples; `a` ties resolve to the lower index.
 __device__ __forceinline__ void merge(float& m, int& a, float& s, float m2, int a2, float s2) {
-  float M = fmaxf(m, m2);
-  if (M == -INFINITY) return;  // both empty
-  float t1 = (m == -INFINITY) ? 0.f : s * tt_exp2((m - M) * LOG2E);
-  float t2 = (m2 == -INFINITY) ? 0.f : s2 * tt_exp2((m2 - M) * LOG2E);
-  int an = (m2 > m) ? a2 : ((m > m2) ? a : min(a, a2));
-  m = M;
-  a = an;
-  s = t1 + t2;
+  tt_merge(m, a, s, m2, a2, s2);
+}
+
+// Merges the records of the workgroup's UM_THREADS threads in a fixed order (butterfly inside each
+// wave, then the waves in increasing order) and stores the result to *out from thread 0.
+__device__ __forceinline__ void wg_merge_store(float m, int a, float s, Partial* out) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    float m2 = tt_shfl_xor(m, off);
+    int a2 = tt_shfl_xor(a, off);
+    float s2 = tt_shfl_xor(s, off);
+    merge(m, a, s, m2, a2, s2);
+  }
+  __shared__ float sm[UM_THREADS / TT_WAVE], ss[UM_THREADS / TT_WAVE];
+  __shared__ int sa[UM_THREADS / TT_WAVE];
+  const int t = threadIdx.x, w = t / TT_WAVE;
+  if ((t & (TT_WAVE - 1)) == 0) {
+    sm[w] = m;
+    ss[w] = s;
+    sa[w] = a;
+  }
+  __syncthreads();
+  if (t == 0) {
+    for (int k = 1; k < UM_THREADS / TT_WAVE; ++k) merge(m, a, s, sm[k], sa[k], ss[k]);
+    Partial p;
+    p.m = m;
+    p.s = s;
+    p.a = a;
+    p.pad = 0;
+    *out = p;
+  }
 }
 
 template <bool VEC4>
@@ -99,32 +120,35 @@ __global__ __launch_bounds__(UM_THREADS) void unmask_partial(const float* __rest
 #pragma unroll
     for (int k = 0; k < UM_PER_THREAD; ++k) s += tt_exp2(fmaf(x[k], LOG2E, -mb));
   }
-  // wave reduction (fixed butterfly order)
+  wg_merge_store(m, a, s, ws + (size_t)r * nchunk + c);
+}
+
+// One workgroup per (block, position) of the fused path: the row's nparts records (one per column
+// block of one LM-head wave) are merged, thread t taking records t, t + 256, ... in increasing
+// order, then across the workgroup in a fixed order; committed positions are skipped.
+constexpr int RM_BATCH = 4;
+__global__ __launch_bounds__(UM_THREADS) void unmask_rowmerge(const Partial* __restrict__ parts,
+                                                              const uint64_t* __restrict__ mask_bits,
+                                                              Partial* __restrict__ rowres, int S,
+                                                              int nparts) {
+  const int r = blockIdx.x;
+  const int b = r / S, i = r - b * S;
+  if (!((mask_bits[b] >> i) & 1ull)) return;
+  const Partial* p = parts + (size_t)r * nparts;
+  float m = -INFINITY, s = 0.f;
+  int a = INT32_MAX;
+  for (int c0 = threadIdx.x; c0 < nparts; c0 += UM_THREADS * RM_BATCH) {
+    Partial x[RM_BATCH];
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    float m2 = tt_shfl_xor(m, off);
-    int a2 = tt_shfl_xor(a, off);
-    float s2 = tt_shfl_xor(s, off);
-    merge(m, a, s, m2, a2, s2);
+    for (int k = 0; k < RM_BATCH; ++k) {
+      const int c = c0 + UM_THREADS * k;
+      if (c < nparts) x[k] = p[c];
+      else x[k] = Partial{-INFINITY, 0.f, INT32_MAX, 0};
+    }
+#pragma unroll
+    for (int k = 0; k < RM_BATCH; ++k) merge(m, a, s, x[k].m, x[k].a, x[k].s);
   }
-  __shared__ float sm[UM_THREADS / TT_WAVE], ss[UM_THREADS / TT_WAVE];
-  __shared__ int sa[UM_THREADS / TT_WAVE];
-  const int w = t / TT_WAVE;
-  if ((t & (TT_WAVE - 1)) == 0) {
-    sm[w] = m;
-    ss[w] = s;
-    sa[w] = a;
-  }
-  __syncthreads();
-  if (t == 0) {
-    for (int k = 1; k < UM_THREADS / TT_WAVE; ++k) merge(m, a, s, sm[k], sa[k], ss[k]);
-    Partial p;
-    p.m = m;
-    p.s = s;
-    p.a = a;
-    p.pad = 0;
-    ws[(size_t)r * nchunk + c] = p;
-  }
+  wg_merge_store(m, a, s, rowres + r);
 }
 
 constexpr int CM_THREADS = 256;
@@ -206,6 +230,18 @@ __global__ __launch_bounds__(CM_THREADS) void unmask_commit(const Partial* __res
   }
 }
 
+// Host checks shared by the two unmask entry points.
+int unmask_check(const int32_t* tokens, const uint64_t* mask_bits, const int32_t* n_masked,
+                 const size_t* workspace_bytes, int B, int S, int V, int step, int num_steps,
+                 float gamma, int mask_id) {
+  if (!tokens || !mask_bits || !n_masked || !workspace_bytes) return TT_ERR_ARG;
+  if (B <= 0 || S <= 0 || V < 2) return TT_ERR_ARG;
+  if (mask_id < 0 || mask_id >= V) return TT_ERR_ARG;
+  if (num_steps <= 0 || step < 0 || step >= num_steps) return TT_ERR_ARG;
+  if (gamma != gamma) return TT_ERR_ARG;
+  return TT_OK;
+}
+
 }  // namespace
 
 extern "C" int tt_confidence_unmask(const float* logits, int32_t* tokens, uint64_t* mask_bits,
@@ -213,17 +249,16 @@ extern "C" int tt_confidence_unmask(const float* logits, int32_t* tokens, uint64
                                     int S, int V, int step, int num_steps, float gamma,
                                     int mask_id, void* workspace, size_t* workspace_bytes,
                                     void* stream) {
-  if (!logits || !tokens || !mask_bits || !n_masked || !workspace_bytes) return TT_ERR_ARG;
-  if (B <= 0 || S <= 0 || V < 2) return TT_ERR_ARG;
-  if (mask_id < 0 || mask_id >= V) return TT_ERR_ARG;
-  if (num_steps <= 0 || step < 0 || step >= num_steps) return TT_ERR_ARG;
-  if (gamma != gamma) return TT_ERR_ARG;
+  if (!logits) return TT_ERR_ARG;
+  int st = unmask_check(tokens, mask_bits, n_masked, workspace_bytes, B, S, V, step, num_steps, gamma,
+                        mask_id);
+  if (st != TT_OK) return st;
   if (S > 64) return TT_ERR_UNSUPPORTED;
   const size_t rows = (size_t)B * S;
   const int nchunk = (V + UM_CHUNK - 1) / UM_CHUNK;
   if (rows * (size_t)nchunk > (size_t)INT32_MAX) return TT_ERR_UNSUPPORTED;
   const size_t need = rows * nchunk * sizeof(Partial);
-  int st = tt_workspace_check(workspace, workspace_bytes, need);
+  st = tt_workspace_check(workspace, workspace_bytes, need);
   if (st != 0) return st < 0 ? st : TT_OK;
   if ((uintptr_t)workspace % alignof(Partial)) return TT_ERR_ARG;
   hipStream_t s = (hipStream_t)stream;
@@ -239,5 +274,41 @@ extern "C" int tt_confidence_unmask(const float* logits, int32_t* tokens, uint64
   if (tt_launch_status() != TT_OK) return TT_ERR_HIP;
   hipLaunchKernelGGL(unmask_commit, dim3(B), dim3(CM_THREADS), 0, s, ws, tokens, mask_bits, n_masked,
                      conf_out, pred_out, S, nchunk, step, num_steps, gamma);
+  return tt_launch_status();
+}
+
+extern "C" int tt_lmhead_unmask(const void* hidden, const void* w, const int32_t* bias_tok,
+                                const float* bias_val, int32_t* tokens, uint64_t* mask_bits,
+                                int32_t* n_masked, float* conf_out, int32_t* pred_out, int B, int S,
+                                int H, int V, int step, int num_steps, float gamma, int mask_id,
+                                int dtype, void* workspace, size_t* workspace_bytes, void* stream) {
+  if (!hidden || !w) return TT_ERR_ARG;
+  if ((bias_tok == nullptr) != (bias_val == nullptr)) return TT_ERR_ARG;
+  int st = unmask_check(tokens, mask_bits, n_masked, workspace_bytes, B, S, V, step, num_steps, gamma,
+                        mask_id);
+  if (st != TT_OK) return st;
+  if (H <= 0) return TT_ERR_ARG;
+  if (dtype != TT_F32 && dtype != TT_BF16) return TT_ERR_UNSUPPORTED;
+  if (dtype != TT_BF16 || H % TT_GEMM_KB != 0 || S > 64) return TT_ERR_UNSUPPORTED;
+  if ((size_t)B * S > (size_t)INT32_MAX) return TT_ERR_UNSUPPORTED;
+  const int M = B * S;
+  const int nparts = tt_lm_reduce_nparts(M, V);
+  if ((size_t)M * nparts > (size_t)INT32_MAX) return TT_ERR_UNSUPPORTED;
+  const size_t parts_bytes = (size_t)M * nparts * sizeof(Partial);
+  const size_t need = parts_bytes + (size_t)M * sizeof(Partial);
+  st = tt_workspace_check(workspace, workspace_bytes, need);
+  if (st != 0) return st < 0 ? st : TT_OK;
+  if ((uintptr_t)workspace % alignof(Partial)) return TT_ERR_ARG;
+  if ((uintptr_t)hidden % 16 || (uintptr_t)w % 16) return TT_ERR_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  Partial* parts = (Partial*)workspace;
+  Partial* rowres = (Partial*)((char*)workspace + parts_bytes);
+  const TtRedArgs red{bias_tok, bias_val, mask_id, parts, nparts};
+  if (tt_lm_reduce_launch(hidden, w, M, H, V, red, s) != TT_OK) return TT_ERR_HIP;
+  hipLaunchKernelGGL(unmask_rowmerge, dim3((unsigned)M), dim3(UM_THREADS), 0, s, parts, mask_bits, rowres,
+                     S, nparts);
+  if (tt_launch_status() != TT_OK) return TT_ERR_HIP;
+  hipLaunchKernelGGL(unmask_commit, dim3(B), dim3(CM_THREADS), 0, s, rowres, tokens, mask_bits, n_masked,
+                     conf_out, pred_out, S, 1, step, num_steps, gamma);
   return tt_launch_status();
 }

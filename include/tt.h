@@ -119,6 +119,35 @@ int tt_confidence_unmask(const float* logits, int32_t* tokens, uint64_t* mask_bi
                          int B, int S, int V, int step, int num_steps, float gamma, int mask_id,
                          void* workspace, size_t* workspace_bytes, void* stream);
 
+/*
+ * tt_lmhead_unmask — tt_lmhead_logits followed by tt_confidence_unmask in one call, with the
+ * vocabulary reduction done in the LM-head kernel's epilogue, so the [B*S][V] logits are never
+ * stored ("Nemotron-Labs-TwoTower" wiki page, section "Block-wise generation": the step needs,
+ * per masked position, only the top probability and its token).
+ *
+ * Computes what tt_confidence_unmask computes on the logits
+ *   l[m][v] = sum_k hidden[m][k] * w[v][k]  (+ bias_val[m] when v == bias_tok[m])
+ * for m = b*S + i. The optional bias adds one value to one vocabulary entry per row (a logit bias
+ * such as a forced or banned token); bias_tok[m] outside [0, V) adds nothing. Both bias
+ * pointers are NULL, or both are device arrays of B*S entries.
+ * Layouts: hidden [B*S][H] bf16, w [V][H] bf16; tokens, mask_bits, n_masked, conf_out,
+ *   pred_out as for tt_confidence_unmask (conf_out / pred_out optional).
+ * Results: equal to the two-call path up to fp32 rounding order of the softmax sum (the logits
+ *   themselves are the same fp32 accumulators); deterministic run to run.
+ * Supported: dtype TT_BF16, H % 64 == 0, 1 <= S <= 64.
+ * Errors: those of tt_confidence_unmask; TT_ERR_ARG also for null hidden / w, H <= 0, exactly one
+ *   bias pointer NULL, hidden or w not 16-byte aligned; TT_ERR_UNSUPPORTED for dtype TT_F32,
+ *   H % 64 != 0 or S > 64.
+ * Workspace: one 16-byte record per (row, block of 32 to 128 vocabulary columns, by B*S) plus one
+ *   per row, sized from B*S and V.
+ */
+int tt_lmhead_unmask(const void* hidden, const void* w, const int32_t* bias_tok,
+                     const float* bias_val, int32_t* tokens, uint64_t* mask_bits,
+                     int32_t* n_masked, float* conf_out, int32_t* pred_out,
+                     int B, int S, int H, int V, int step, int num_steps, float gamma,
+                     int mask_id, int dtype, void* workspace, size_t* workspace_bytes,
+                     void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* tt_status_string(int status);
 

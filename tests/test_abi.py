@@ -126,3 +126,39 @@ def test_unmask_argument_errors(kw, code):
 def test_unmask_any_gamma_is_legal():
     for g in (float("inf"), float("-inf"), 2.0, 0.0, -1.0):
         assert _um(gamma=g)[0] == 0
+
+
+def _fu(ws=None, nbytes=0, **kw):
+    a = dict(h=P, w=P, bt=None, bv=None, tok=P, bits=P, nm=P, B=1, S=16, H=2688, V=131072, step=0, T=16,
+             gamma=0.8, mask_id=3, dtype=_lib.TT_BF16)
+    a.update(kw)
+    n = ctypes.c_size_t(nbytes)
+    st = _lib.load().tt_lmhead_unmask(a["h"], a["w"], a["bt"], a["bv"], a["tok"], a["bits"], a["nm"], None, None,
+                                      a["B"], a["S"], a["H"], a["V"], a["step"], a["T"], a["gamma"],
+                                      a["mask_id"], a["dtype"], ws, ctypes.byref(n), None)
+    return st, n.value
+
+
+def test_fused_workspace_query():
+    # records per row: 64 columns each for up to 16 rows, 32 for up to 64, 128 beyond; plus one per row
+    for B, cols in ((1, 64), (4, 32), (5, 128), (32, 128)):
+        M = 16 * B
+        st, n = _fu(B=B)
+        assert st == 0 and n == M * (131072 // cols) * 16 + M * 16, (B, n)
+    st, n = _fu(V=1000)
+    assert st == 0 and n == 16 * 16 * 16 + 16 * 16      # ceil(1000 / 64) = 16 records per row
+    assert _fu(ws=P, nbytes=10)[0] == _lib.TT_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(h=None), -1), (dict(w=None), -1), (dict(tok=None), -1), (dict(bits=None), -1), (dict(nm=None), -1),
+    (dict(bt=P), -1), (dict(bv=P), -1), (dict(B=0), -1), (dict(S=0), -1), (dict(H=0), -1), (dict(V=1), -1),
+    (dict(mask_id=131072), -1), (dict(step=16), -1), (dict(gamma=float("nan")), -1),
+    (dict(dtype=_lib.TT_F32), -2), (dict(dtype=7), -2), (dict(H=2656), -2), (dict(S=65), -2),
+])
+def test_fused_argument_errors(kw, code):
+    assert _fu(**kw)[0] == code
+
+
+def test_fused_bias_pair_accepted():
+    assert _fu(bt=P, bv=P)[0] == 0

@@ -49,7 +49,10 @@ def _run_and_compare(wl, logits_np, steps, gamma=None, state=None):
         ref = oracle.confidence_unmask(logits_np, tokens_h, bits_h, wl.S, step, wl.T, gamma, wl.mask_id)
         g = _gpu_step(logits_d, tokens_d, bits_d, wl.S, step, wl.T, gamma, wl.mask_id)
         exempt += check_commit_step(wl.S, gamma, step, wl.T, bits_h, tokens_h, g, ref)
-        tokens_h, bits_h = g["tokens"], g["mask_bits"]  # continue from the GPU state (equal unless exempt)
+        # both sides continue from the oracle's state (the GPU's equals it unless exempt)
+        tokens_h, bits_h = ref["tokens"], ref["mask_bits"]
+        tokens_d.copy_(dev(tokens_h))
+        bits_d.copy_(dev(bits_h))
     return exempt, tokens_h, bits_h
 
 
