@@ -31,13 +31,24 @@ __device__ __forceinline__ int mrow(int lane, int j) { return 8 * (j >> 2) + 4 *
 // rows (2 x 2 waves); with two hidden-row blocks the workgroups of one vocabulary tile have
 // dispatch ids congruent modulo 8 (same XCD) and 8 apart, so W is fetched from HBM once (measured
 // with FETCH_SIZE). A 512 x 128 tile (W read by one workgroup only) measured slower: it doubles
-// the re-reads of the hidden rows from L2.
-constexpr int GM_KB = TT_GEMM_KB, GM_NBUF = 2;
-constexpr int GM_ROWB = GM_KB * 2;                  // bytes per LDS row (one cache line)
+// the re-reads of the hidden rows from L2. Also measured and not faster at 512 rows: 32-wide
+// stages in a 4- or 5-deep ring (TT_GEMM_KB=32, TT_GM_NBUF=4 or 5 build the variant), the LDS
+// reads pinned between the MFMAs of the previous k-step, and a per-workgroup rotation of the
+// k-stage order.
+#ifndef TT_GM_NBUF
+#define TT_GM_NBUF 2
+#endif
+constexpr int GM_KB = TT_GEMM_KB, GM_NBUF = TT_GM_NBUF;
+constexpr int GM_ROWB = GM_KB * 2;                  // bytes per LDS row
 constexpr int GM_KS = GM_KB / 16;                   // MFMA k-steps per stage
-static_assert(GM_ROWB == 128, "ring geometry");
+constexpr int GM_GPR = GM_KB / 8;                   // 16-byte granules per row
+constexpr int GM_RPC = 1024 / GM_ROWB;              // rows per 1 KiB load chunk (64 lanes x 16 B)
+static_assert(GM_KB == 32 || GM_KB == 64, "stage width");
+static_assert(GM_KS % 2 == 0, "k-steps are pipelined in pairs");
 
-__device__ __forceinline__ int gm_swz(int r) { return (r >> 1) & 7; }
+// granule slot permutation of row r: the 16 rows read by 16 consecutive lanes (one 256-byte
+// LDS bank sweep) land in 16 distinct 16-byte bank groups
+__device__ __forceinline__ int gm_swz(int r) { return (r / (256 / GM_ROWB)) % GM_GPR; }
 
 // WM waves along the hidden rows, 4 / WM along the vocabulary, each owning a 128 x 128 block:
 // tile BM = 128 WM hidden rows x BN = 128 (4 / WM) vocabulary rows.
@@ -52,10 +63,13 @@ __global__ __launch_bounds__(LM_THREADS, 1) __attribute__((amdgpu_waves_per_eu(1
   constexpr int GM_BM = 128 * WM, GM_BN = 128 * WN;
   constexpr int ASTAGE = GM_BM * GM_ROWB, BSTAGE = GM_BN * GM_ROWB;  // bytes per stage
   constexpr int ACPW = ASTAGE / 1024 / LM_WAVES, BCPW = BSTAGE / 1024 / LM_WAVES;  // chunks per wave
+  constexpr int PER_STAGE = ACPW + BCPW;  // load instructions per wave and stage
+  // ring depth: as deep as asked, within the LDS of one workgroup
+  constexpr int NBUF = GM_NBUF * (ASTAGE + BSTAGE) <= 160 * 1024 ? GM_NBUF : 160 * 1024 / (ASTAGE + BSTAGE);
+  static_assert(NBUF >= 2 && (NBUF - 2) * PER_STAGE <= 63, "ring depth");
   typedef bf16x8 frag;
-  __shared__ __attribute__((aligned(16))) unsigned char sa[GM_NBUF][ASTAGE];
-  __shared__ __attribute__((aligned(16))) unsigned char sb[GM_NBUF][BSTAGE];
-  static_assert(GM_NBUF * (ASTAGE + BSTAGE) <= 160 * 1024, "LDS per workgroup");
+  __shared__ __attribute__((aligned(16))) unsigned char sa[NBUF][ASTAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char sb[NBUF][BSTAGE];
 
   const int id = blockIdx.x;
   const int grp = id / (NXCD * nmb);
@@ -69,26 +83,27 @@ __global__ __launch_bounds__(LM_THREADS, 1) __attribute__((amdgpu_waves_per_eu(1
   const int wm = wave / WN, wn = wave % WN;
   const int m0 = mblk * GM_BM, v0 = vtile * GM_BN;
 
-  // load sources: chunk c = wave * CPW + i covers tile rows [8c, 8c + 8); lane -> row
-  // 8c + lane / 8, LDS slot lane % 8, which holds logical granule slot ^ swz(row). Rows past M
-  // or V re-read the last row (in bounds; their results are never stored).
+  // load sources: chunk c = wave * CPW + i covers tile rows [RPC c, RPC (c + 1)); lane -> row
+  // RPC c + lane / GPR, LDS slot lane % GPR, which holds logical granule slot ^ swz(row). Rows
+  // past M or V re-read the last row (in bounds; their results are never stored).
   const bf16* asrc[ACPW];
   const bf16* bsrc[BCPW];
 #pragma unroll
   for (int i = 0; i < ACPW; ++i) {
-    const int r = (wave * ACPW + i) * 8 + lane / 8;
-    asrc[i] = hidden + (size_t)min(m0 + r, M - 1) * H + 8 * ((lane & 7) ^ gm_swz(r));
+    const int r = (wave * ACPW + i) * GM_RPC + lane / GM_GPR;
+    asrc[i] = hidden + (size_t)min(m0 + r, M - 1) * H + 8 * ((lane % GM_GPR) ^ gm_swz(r));
   }
 #pragma unroll
   for (int i = 0; i < BCPW; ++i) {
-    const int r = (wave * BCPW + i) * 8 + lane / 8;
-    bsrc[i] = w + (size_t)min(v0 + r, V - 1) * H + 8 * ((lane & 7) ^ gm_swz(r));
+    const int r = (wave * BCPW + i) * GM_RPC + lane / GM_GPR;
+    bsrc[i] = w + (size_t)min(v0 + r, V - 1) * H + 8 * ((lane % GM_GPR) ^ gm_swz(r));
   }
   // this wave's first LDS slot of stage buffer 0 in each ring; the rest are constant offsets
   const uint32_t a_lds = tt_lds_addr(&sa[0][wave * ACPW * 1024]);
   const uint32_t b_lds = tt_lds_addr(&sb[0][wave * BCPW * 1024]);
+  const int nst = H / GM_KB;
   auto issue = [&](int st) {
-    const int buf = st % GM_NBUF, k0 = st * GM_KB;
+    const int buf = st % NBUF, k0 = st * GM_KB;
     const uint32_t ab = a_lds + buf * ASTAGE, bb = b_lds + buf * BSTAGE;
     tt_static_for<ACPW>([&](auto i) { tt_dma16_at<i * 1024>(asrc[i] + k0, ab); });
     tt_static_for<BCPW>([&](auto i) { tt_dma16_at<i * 1024>(bsrc[i] + k0, bb); });
@@ -123,16 +138,21 @@ __global__ __launch_bounds__(LM_THREADS, 1) __attribute__((amdgpu_waves_per_eu(1
                           : __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mt], fb[nt], acc[mt][nt], 0, 0, 0);
   };
 
-  // Stage st: wait for this wave's loads of it (the only ones outstanding), barrier (every
-  // wave's loads are in LDS and stage st - 1 has been read by all), refill the other buffer with
-  // stage st + 1, then GM_KS k-steps with the fragments of step ks + 1 read during step ks.
-  const int nst = H / GM_KB;
-  issue(0);
+  // Stage st: wait for this wave's loads of it (those of the NBUF - 2 later stages may still
+  // be in flight), barrier (every wave's loads of stage st are in LDS and every wave has read
+  // stage st - 1), refill stage st - 1's buffer with stage st + NBUF - 1, then GM_KS k-steps
+  // with the fragments of step ks + 1 read during step ks.
+#pragma unroll
+  for (int e = 0; e < NBUF - 1; ++e)
+    if (e < nst) issue(e);
   for (int st = 0; st < nst; ++st) {
-    tt_wait_vmem<0>();
+    const int later = min(nst - 1 - st, NBUF - 2);  // stages issued after st, in flight
+    tt_static_for<NBUF - 1>([&](auto n) {
+      if (later == n) tt_wait_vmem<n * PER_STAGE>();
+    });
     tt_lds_barrier();
-    if (st + 1 < nst) issue(st + 1);
-    const int buf = st % GM_NBUF;
+    if (st + NBUF - 1 < nst) issue(st + NBUF - 1);
+    const int buf = st % NBUF;
     frag fa0[4], fb0[4], fa1[4], fb1[4];
     read_frags(buf, 0, fa0, fb0);
 #pragma unroll
