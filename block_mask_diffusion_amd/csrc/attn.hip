@@ -20,6 +20,13 @@
 // only. The exponentials are written back into the same registers and used directly as the B
 // operand of O^T = V^T P^T; the V^T operand is read from the row-major V stage with transposing
 // LDS reads, in the key order of the score registers.
+//
+// What bounds it (MI355X counters at 4 x 131072 keys): the LDS pipe, active about 94% of the
+// kernel's time. Each of the 8 waves reads the whole K and V of every stage (8 KiB each per 32
+// keys; the V^T reads are 64-bit transposing reads, so V costs twice K's instructions). Two
+// query tiles per wave halve that traffic but leave one wave per SIMD and, as compiled, move the
+// output accumulators between register files every sub-tile: slower. Issuing the second
+// sub-tile's score MFMAs before the first one's softmax did not change the time either.
 #include "common.h"
 
 namespace {
@@ -39,6 +46,11 @@ constexpr int AT_MAX_B = 1024;  // sequences handled by the in-workgroup prefix 
 constexpr float LOG2E = 1.4426950408889634f;
 static_assert(MAX_ROWS == QT * TPW * AT_WAVES, "8 query tiles per workgroup");
 constexpr float RESCALE_LOG2 = 8.f;  // lazy-rescale threshold (log2 units)
+// K/V stage loads: every key row is read exactly once, so they stream with the non-temporal
+// policy
+#ifndef TT_AT_DMA
+#define TT_AT_DMA tt_dma16_nt
+#endif
 
 template <typename T>
 struct Mf;
@@ -311,7 +323,7 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_partial(Args<T, D> A) {
       const int chunk = wave * CPW + c;
       unsigned char* dst = kv ? &ring.v[buf][chunk * 1024] : &ring.k[buf][chunk * 1024];
       if (k0 + KC <= fast_end) {
-        tt_dma16((kv ? vfast[c] : kfast[c]) + (size_t)st * KC * RB, tt_lds_addr(dst));
+        TT_AT_DMA((kv ? vfast[c] : kfast[c]) + (size_t)st * KC * RB, tt_lds_addr(dst));
         return;
       }
       const int r = chunk * GE::RPC + lane / GPR, slot = lane % GPR;
@@ -320,7 +332,7 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_partial(Args<T, D> A) {
       const int g = slot ^ (kv ? GE::fv(r) : GE::fk(r));
       const T* src = kv ? (key < P ? vctx + (size_t)key * D : vblk + (size_t)(key - P) * blk_stride)
                         : (key < P ? kctx + (size_t)key * D : kblk + (size_t)(key - P) * blk_stride);
-      tt_dma16(reinterpret_cast<const unsigned char*>(src) + 16 * g, tt_lds_addr(dst));
+      TT_AT_DMA(reinterpret_cast<const unsigned char*>(src) + 16 * g, tt_lds_addr(dst));
     };
     auto issue_stage = [&](int st) {
 #pragma unroll
@@ -454,7 +466,6 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_partial(Args<T, D> A) {
     for (int st = 0; st < PD; ++st)
       if (st < nst) issue_stage(st);
 
-    // one sub-tile: scores, softmax, and (unless deferred) the PV product
     // one sub-tile: scores, softmax and the PV product
     auto subtile = [&](int st, int kt) {
       const int kvalid = nkeys - st * KC - kt * 32;  // keys of this sub-tile that exist
