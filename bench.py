@@ -59,7 +59,8 @@ def algorithmic(wl):
     return dict(attn_bytes=attn_bytes, attn_flops=attn_flops, lm_bytes=lm_bytes, lm_flops=lm_flops)
 
 
-TRAFFIC_SOURCES = {"lmhead": ("lmhead.hip", "common.h"), "attn": ("attn.hip", "common.h")}
+TRAFFIC_SOURCES = {"lmhead": ("lmhead.hip", "lmhead_int.h", "reduce_int.h", "common.h"),
+                   "attn": ("attn.hip", "common.h")}
 
 
 def read_traffic(kind, wid):
@@ -80,8 +81,9 @@ def read_traffic(kind, wid):
 
 
 def source_hash(kind):
-    """sha256 of a kernel's code (its .hip file + common.h) with // comments, trailing blanks and
-    blank lines removed, so that editing a comment does not void a traffic record."""
+    """sha256 of a kernel's code (its .hip file and the headers it includes) with // comments,
+    trailing blanks and blank lines removed, so that editing a comment does not void a traffic
+    record."""
     import hashlib
     import re
     h = hashlib.sha256()
