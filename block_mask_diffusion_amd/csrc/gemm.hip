@@ -83,15 +83,59 @@ __global__ __launch_bounds__(LM_THREADS, 1) __attribute__((amdgpu_waves_per_eu(1
   const int wm = wave / WN, wn = wave % WN;
   const int m0 = mblk * GM_BM, v0 = vtile * GM_BN;
 
+  // Fused mode with a mask, on the two-m-block tile: only the still-masked rows are multiplied.
+  // Every workgroup compacts the masked rows (ascending) from the mask words itself, and its
+  // m-block takes compacted rows [m0, m0 + BM); m-blocks past the last masked row exit. Tile row
+  // r is hidden row rowmap[r]. (The 128-row tile has no LDS to spare and needs one m-block for
+  // up to 128 rows anyway.)
+  constexpr bool GATHER = RED && WM == 2;
+  __shared__ int rowmap[GATHER ? GM_BM : 1];
+  int nrows = M - m0;  // valid tile rows; rows past them re-read a valid row, results unused
+  if constexpr (GATHER) {
+    if (red.mask_bits) {
+      __shared__ int scan[LM_THREADS];
+      int base = 0;
+      for (int b0 = 0; b0 < red.B; b0 += LM_THREADS) {
+        const int b = b0 + tid;
+        uint64_t bits = b < red.B ? red.mask_bits[b] : 0ull;
+        const int c = __popcll(bits);
+        scan[tid] = c;
+        __syncthreads();
+        for (int off = 1; off < LM_THREADS; off <<= 1) {  // inclusive scan of the counts
+          const int x = tid >= off ? scan[tid - off] : 0;
+          __syncthreads();
+          scan[tid] += x;
+          __syncthreads();
+        }
+        int k = base + scan[tid] - c;  // compacted index of block b's first masked row
+        const int total = scan[LM_THREADS - 1];
+        while (bits) {
+          const int i = __builtin_ctzll(bits);
+          bits &= bits - 1;
+          if (k >= m0 && k < m0 + GM_BM) rowmap[k - m0] = b * red.S + i;
+          ++k;
+        }
+        base += total;
+        __syncthreads();  // scan[] is reused by the next chunk of blocks
+      }
+      nrows = base - m0;
+    } else {
+      for (int r = tid; r < GM_BM; r += LM_THREADS) rowmap[r] = min(m0 + r, M - 1);
+    }
+    __syncthreads();
+    if (nrows <= 0) return;  // the same for every thread
+  }
+  auto hrow = [&](int r) { return GATHER ? rowmap[min(r, nrows - 1)] : min(m0 + r, M - 1); };
+
   // load sources: chunk c = wave * CPW + i covers tile rows [RPC c, RPC (c + 1)); lane -> row
   // RPC c + lane / GPR, LDS slot lane % GPR, which holds logical granule slot ^ swz(row). Rows
-  // past M or V re-read the last row (in bounds; their results are never stored).
+  // past M (or the masked rows) or V re-read a valid row (in bounds; results never stored).
   const bf16* asrc[ACPW];
   const bf16* bsrc[BCPW];
 #pragma unroll
   for (int i = 0; i < ACPW; ++i) {
     const int r = (wave * ACPW + i) * GM_RPC + lane / GM_GPR;
-    asrc[i] = hidden + (size_t)min(m0 + r, M - 1) * H + 8 * ((lane % GM_GPR) ^ gm_swz(r));
+    asrc[i] = hidden + (size_t)hrow(r) * H + 8 * ((lane % GM_GPR) ^ gm_swz(r));
   }
 #pragma unroll
   for (int i = 0; i < BCPW; ++i) {
@@ -181,7 +225,7 @@ __global__ __launch_bounds__(LM_THREADS, 1) __attribute__((amdgpu_waves_per_eu(1
     bool hit = false;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      const int mc = min(m0 + 128 * wm + 32 * mt + l32, M - 1);
+      const int mc = hrow(128 * wm + 32 * mt + l32);
       btok[mt] = red.bias_tok ? red.bias_tok[mc] : -1;
       bval[mt] = red.bias_tok ? red.bias_val[mc] : 0.f;
       hit = hit || (btok[mt] >= cb && btok[mt] < cb + 128);
@@ -255,8 +299,9 @@ __global__ __launch_bounds__(LM_THREADS, 1) __attribute__((amdgpu_waves_per_eu(1
           for (int q = 0; q < w2; ++q) sm[q] += sm[q + w2];
         const float rs = sm[0] + tt_swap_halves(sm[0]);  // same sum on both halves (commutative)
         key = min(key, tt_swap_halves_i(key));
-        const int m = m0 + 128 * wm + 32 * mt + l32;
-        if (hh == 0 && m < M) {
+        const int rr = 128 * wm + 32 * mt + l32;
+        if (hh == 0 && rr < nrows) {
+          const int m = GATHER ? rowmap[rr] : m0 + rr;
           TtPartial p;
           p.m = rm;
           p.s = rs;

@@ -34,6 +34,10 @@ struct TtRedArgs {
   int mask_id;              // never a candidate (its logit counts as -inf)
   TtPartial* parts;         // [M][nparts]: one record per (row, column block of one wave)
   int nparts;
+  // optional: only rows b * S + i with bit i of mask_bits[b] set need a record (kernels that
+  // can skip the other rows do; NULL = every row)
+  const uint64_t* mask_bits;
+  int S, B;
 };
 
 // Cross-lane partner values for a butterfly over groups of up to 32 consecutive lanes, all on

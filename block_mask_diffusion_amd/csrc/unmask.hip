@@ -303,7 +303,7 @@ extern "C" int tt_lmhead_unmask(const void* hidden, const void* w, const int32_t
   hipStream_t s = (hipStream_t)stream;
   Partial* parts = (Partial*)workspace;
   Partial* rowres = (Partial*)((char*)workspace + parts_bytes);
-  const TtRedArgs red{bias_tok, bias_val, mask_id, parts, nparts};
+  const TtRedArgs red{bias_tok, bias_val, mask_id, parts, nparts, mask_bits, S, B};
   if (tt_lm_reduce_launch(hidden, w, M, H, V, red, s) != TT_OK) return TT_ERR_HIP;
   hipLaunchKernelGGL(unmask_rowmerge, dim3((unsigned)M), dim3(UM_THREADS), 0, s, parts, mask_bits, rowres,
                      S, nparts);

@@ -226,3 +226,50 @@ def test_fp32_inputs_are_unsupported():
     nm = torch.empty(1, dtype=torch.int32, device="cuda")
     with pytest.raises(bmd.TTError):
         bmd.tt_lmhead_unmask(h, w, dev(st["tokens"]), dev(st["mask_bits"]), nm, 0, 16, 0.8, 3)
+
+
+def test_fused_gemm_masked_rows_only_with_nan_committed_rows():
+    """More than 128 rows: the product runs over the still-masked rows only (compacted in the
+    kernel); committed rows' hidden states may hold NaN. Several steps, so the masked count
+    crosses the 256-row tile boundary."""
+    wl = _wl(28, 16, 128, 1500, partial=True, salt=21)
+    inp = synth.lmhead_inputs(wl)
+    st = synth.initial_state(wl)
+    bt, bv = _bias(wl)
+    lg = _oracle_logits(inp, bt, bv)
+    tokens_h, bits_h = st["tokens"].copy(), st["mask_bits"].copy()
+    hid = inp["hidden"].copy()
+    for b in range(wl.B):
+        for i in range(wl.S):
+            if not (int(bits_h[b]) >> i) & 1:
+                hid[b * wl.S + i] = 0x7FC0     # bf16 quiet NaN in rows committed before step 0
+    hid_d, w_d, bt_d, bv_d = dev(hid), dev(inp["w"]), dev(bt), dev(bv)
+    tok_d, bits_d = dev(tokens_h), dev(bits_h)
+    counts = []
+    for step in range(6):
+        counts.append(sum(bin(int(x)).count("1") for x in bits_h))
+        ref = oracle.confidence_unmask(lg, tokens_h, bits_h, wl.S, step, wl.T, wl.gamma, wl.mask_id)
+        g = _fused(hid_d, w_d, bt_d, bv_d, tok_d, bits_d, wl.B, wl.S, step, wl.T, wl.gamma, wl.mask_id)
+        check_fused_step(wl.S, wl.gamma, step, wl.T, bits_h, g, ref, lambda m: lg[m], wl.mask_id, range(wl.B))
+        tokens_h, bits_h = ref["tokens"], ref["mask_bits"]
+        tok_d.copy_(dev(tokens_h))
+        bits_d.copy_(dev(bits_h))
+    assert counts[0] > 256 and min(counts) < 256
+
+
+def test_fused_gemm_nothing_masked():
+    wl = _wl(18, 16, 64, 700, salt=22)
+    inp = synth.lmhead_inputs(wl)
+    tokens = np.arange(wl.M, dtype=np.int32).reshape(wl.B, wl.S) % wl.V
+    tokens[tokens == wl.mask_id] = 0
+    bits = np.zeros(wl.B, np.uint64)
+    g = _fused(dev(inp["hidden"]), dev(inp["w"]), None, None, dev(tokens), dev(bits), wl.B, wl.S, 0, wl.T,
+               wl.gamma, wl.mask_id)
+    assert np.array_equal(g["tokens"], tokens) and np.all(g["mask_bits"] == 0) and np.all(g["n_masked"] == 0)
+    assert np.all(g["conf"] == -1.0) and np.all(g["pred"] == -1)
+
+
+def test_fused_gemm_full_block_to_completion():
+    wl = _wl(20, 16, 64, 900, salt=23)
+    _, _, tokens, bits = _steps(wl, wl.T)
+    assert np.all(bits == 0) and np.all(tokens != wl.mask_id)
