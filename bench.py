@@ -272,6 +272,38 @@ def main():
     total_ms_fu = start_fu.elapsed_time(end_fu)
     t_fu = sum(e[1].elapsed_time(e[2]) for e in evs_fu) / K
 
+    # the context tower's step over a committed block (once per block in the outer loop, not part
+    # of the denoiser step): one layer's tt_context_extend on layer 0's cache, laid out again with
+    # room for S more rows per sequence; ctx_len is restored before every call
+    a0 = attn_d[0]
+    cap = torch.from_numpy(np.asarray(wl.prefixes, dtype=np.int64) + wl.S)
+    ext_start = (torch.cumsum(cap, 0) - cap).to(torch.int32).to(dev)
+    rows_old = torch.cat([torch.arange(int(s0), int(s0) + p) for s0, p in zip(wl.ctx_start, wl.prefixes)])
+    rows_new = torch.cat([torch.arange(int(s0), int(s0) + p) for s0, p in zip(ext_start.cpu(), wl.prefixes)])
+    R2 = int(cap.sum())
+    kc2 = torch.zeros((wl.Hkv, R2, wl.D), dtype=a0["k_ctx"].dtype, device=dev)
+    vc2 = torch.zeros_like(kc2)
+    kc2[:, rows_new.to(dev)] = a0["k_ctx"][:, rows_old.to(dev)]
+    vc2[:, rows_new.to(dev)] = a0["v_ctx"][:, rows_old.to(dev)]
+    len0 = a0["ctx_len"].clone()
+    ext_len = len0.clone()
+    ext_out = torch.empty_like(a0["q"])
+    ws_ext = torch.empty(bmd.workspace_bytes("tt_block_attn", B=wl.B, S=wl.S, Hq=wl.Hq, Hkv=wl.Hkv, D=wl.D,
+                                             ctx_rows=R2, max_prefix=wl.max_prefix), dtype=torch.uint8, device=dev)
+    t_ext = []
+    for i in range(4 + 8):
+        ext_len.copy_(len0)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        bmd.tt_context_extend(a0["q"], a0["k_blk"], a0["v_blk"], kc2, vc2, ext_start, ext_len,
+                              max_prefix=wl.max_prefix, softmax_scale=a0["scale"], out=ext_out, workspace=ws_ext)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if i >= 4:
+            t_ext.append(e0.elapsed_time(e1))
+    t_ext = sum(t_ext) / len(t_ext)
+    del kc2, vc2
+
     t_attn = sum(e[0].elapsed_time(e[1]) for e in evs) / K
     t_lm = sum(e[1].elapsed_time(e[2]) for e in evs) / K
     t_spk = sum(e[2].elapsed_time(e[3]) for e in evs) / K
@@ -295,6 +327,8 @@ def main():
     sec_fu = total_ms_fu / 1e3
     alg = algorithmic(wl)
     lm_gbs = alg["lm_bytes"] / (t_lm / 1e3) / 1e9
+    # context extend: the attention's bytes plus the appended rows written
+    ext_bytes = alg["attn_bytes"] + (2 if wl.dtype == "bf16" else 4) * 2.0 * wl.B * wl.S * wl.Hkv * wl.D
     t_attn_call = t_attn / wl.layers  # ms per tt_block_attn call (one layer)
     attn_gbs = alg["attn_bytes"] / (t_attn_call / 1e3) / 1e9
     um_bytes = 4.0 * wl.V * masked_rows / K
@@ -372,6 +406,13 @@ def main():
             "lmhead_unmask_us": round(t_fu * 1e3, 2),
             "lmhead_unmask_hbm_frac": round((alg["lm_bytes"] - 4.0 * wl.M * wl.V) / (t_fu / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
             "lmhead_unmask_mfma_frac": round(alg["lm_flops"] / (t_fu / 1e3) / 1e12 / MFMA_BF16_PEAK_TFS, 4),
+        },
+        "context_extend": {
+            "what": "tt_context_extend, one layer: causal attention of the S committed tokens over "
+                    "[cache ; block], then the append of their K/V (once per block, not in the step)",
+            "us": round(t_ext * 1e3, 2),
+            "GB_s": round(ext_bytes / (t_ext / 1e3) / 1e9, 1),
+            "hbm_frac": round(ext_bytes / (t_ext / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
         },
         "wall_s_timed": round(wall, 3),
         "input_gen_s": round(gen_s, 1),

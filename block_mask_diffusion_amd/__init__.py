@@ -15,8 +15,8 @@ import torch
 from . import _lib
 from ._lib import TTError, TT_BF16, TT_F32
 
-__all__ = ["tt_block_attn", "tt_lmhead_logits", "tt_confidence_unmask", "tt_lmhead_unmask",
-           "workspace_bytes", "TTError", "abi_version"]
+__all__ = ["tt_block_attn", "tt_context_extend", "tt_lmhead_logits", "tt_confidence_unmask",
+           "tt_lmhead_unmask", "workspace_bytes", "TTError", "abi_version"]
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -121,6 +121,40 @@ def tt_block_attn(q: torch.Tensor, k_blk: torch.Tensor, v_blk: torch.Tensor,
     ws = _workspace(n.value, workspace, q.device)
     n2 = ctypes.c_size_t(ws.numel() * ws.element_size())
     _check(lib.tt_block_attn(*args, _ptr(ws), ctypes.byref(n2), _stream(stream)), "tt_block_attn")
+    return out
+
+
+def tt_context_extend(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                      k_ctx: torch.Tensor, v_ctx: torch.Tensor, ctx_start: torch.Tensor,
+                      ctx_len: torch.Tensor, max_prefix: int, softmax_scale: Optional[float] = None,
+                      out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                      stream=None) -> torch.Tensor:
+    """The context tower's causal attention over a committed block, then the append of k_new /
+    v_new to the cache (k_ctx, v_ctx and ctx_len updated in place; see include/tt.h). Shapes as
+    tt_block_attn with k_new / v_new [B][S][Hkv][D]."""
+    _need(q.dim() == 4 and k_new.dim() == 4 and v_new.dim() == 4, "q, k_new, v_new are 4-d")
+    B, S, Hq, D = q.shape
+    Hkv = k_new.shape[2]
+    _need(tuple(k_new.shape) == (B, S, Hkv, D) and tuple(v_new.shape) == (B, S, Hkv, D), "new K/V shape")
+    _need(k_ctx.dim() == 3 and tuple(k_ctx.shape) == tuple(v_ctx.shape), "context K/V shape")
+    _need(k_ctx.shape[0] == Hkv and k_ctx.shape[2] == D, "context K/V shape")
+    _need(ctx_start.dtype == torch.int32 and ctx_len.dtype == torch.int32, "ctx_start/ctx_len are int32")
+    _need(ctx_start.numel() == B and ctx_len.numel() == B, "ctx_start/ctx_len have B entries")
+    for t in (k_new, v_new, k_ctx, v_ctx):
+        _need(t.dtype == q.dtype, "all attention tensors share one dtype")
+    _dev(q, k_new, v_new, k_ctx, v_ctx, ctx_start, ctx_len, out)
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out)
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    lib = _lib.load()
+    n = ctypes.c_size_t(0)
+    args = [_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_ctx), _ptr(v_ctx), _ptr(ctx_start), _ptr(ctx_len),
+            _ptr(out), B, S, Hq, Hkv, D, k_ctx.shape[1], int(max_prefix), scale, _dtype(q)]
+    _check(lib.tt_context_extend(*args, None, ctypes.byref(n), None), "tt_context_extend")
+    ws = _workspace(n.value, workspace, q.device)
+    n2 = ctypes.c_size_t(ws.numel() * ws.element_size())
+    _check(lib.tt_context_extend(*args, _ptr(ws), ctypes.byref(n2), _stream(stream)), "tt_context_extend")
     return out
 
 

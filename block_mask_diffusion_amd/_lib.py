@@ -21,8 +21,8 @@ TT_F32, TT_BF16 = 0, 1
 TT_OK, TT_ERR_ARG, TT_ERR_UNSUPPORTED, TT_ERR_WORKSPACE, TT_ERR_HIP = 0, -1, -2, -3, -4
 
 # every symbol include/tt.h declares
-EXPORTS = ("tt_block_attn", "tt_lmhead_logits", "tt_confidence_unmask", "tt_lmhead_unmask",
-           "tt_status_string", "tt_abi_version")
+EXPORTS = ("tt_block_attn", "tt_context_extend", "tt_lmhead_logits", "tt_confidence_unmask",
+           "tt_lmhead_unmask", "tt_status_string", "tt_abi_version")
 
 _lib = None
 
@@ -58,6 +58,8 @@ def load() -> ctypes.CDLL:
     vp, i, i64, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.POINTER(ctypes.c_size_t)
     lib.tt_block_attn.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i64, i, f32, i, vp, sz, vp]
     lib.tt_block_attn.restype = i
+    lib.tt_context_extend.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i64, i, f32, i, vp, sz, vp]
+    lib.tt_context_extend.restype = i
     lib.tt_lmhead_logits.argtypes = [vp, vp, vp, i, i, i, i, vp]
     lib.tt_lmhead_logits.restype = i
     lib.tt_confidence_unmask.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f32, i, vp, sz, vp]

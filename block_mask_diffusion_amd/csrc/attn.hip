@@ -210,7 +210,10 @@ struct Args {
 
 #define LDS_PTR(T, p) TT_LDS_PTR(T, p)
 
-template <typename T, int D>
+// CAUSAL = false: the denoiser's block attention (bidirectional in the block).
+// CAUSAL = true: the context tower's step over newly committed tokens: block row j is visible to
+// block position s only for j <= s (the prefix is visible to every position).
+template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(AT_THREADS, 1) void attn_partial(Args<T, D> A) {
   typedef Mf<T> MF;
   typedef Geo<T, D> GE;
@@ -408,13 +411,22 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_partial(Args<T, D> A) {
 
     // softmax of one sub-tile's scores (in place) -> bf16/fp32 probabilities pf; updates the
     // running max (lazy rescale of o and l) and the running sum l
-    auto softmax = [&](f32x16 (&sacc)[TPW], int kvalid, frag (&pf)[TPW][32 / KS]) {
+    // kfirst: index in the unit's key list of the sub-tile's first key
+    auto softmax = [&](f32x16 (&sacc)[TPW], int kvalid, int kfirst, frag (&pf)[TPW][32 / KS]) {
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
         if (kvalid < 32) {
 #pragma unroll
           for (int j = 0; j < 16; ++j)
             if (8 * (j >> 2) + 4 * hh2 + (j & 3) >= kvalid) sacc[t][j] = -INFINITY;
+        }
+        if constexpr (CAUSAL) {
+          if (kfirst + 32 > P) {  // the sub-tile reaches the block rows: mask j > s
+            const int srow = ((wave * TPW + t) * QT + l32) / G;
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+              if (kfirst + 8 * (j >> 2) + 4 * hh2 + (j & 3) - P > srow) sacc[t][j] = -INFINITY;
+          }
         }
         float mx = fmaxf(fmaxf(sacc[t][0], sacc[t][1]), sacc[t][2]);
 #pragma unroll
@@ -425,7 +437,9 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_partial(Args<T, D> A) {
         // 2^8 in the exponent; exponentials stay <= 256 and the final normalisation is exact.
         if (__ballot((mx - mrun[t]) * A.c > RESCALE_LOG2)) {
           const float mnew = fmaxf(mrun[t], mx);
-          const float alpha = tt_exp2((mrun[t] - mnew) * A.c);  // 0 on the first update
+          // 0 on the first update; 1 for a row that has seen no visible key yet (causal), where
+          // both maxima are -inf and their difference would be NaN
+          const float alpha = (CAUSAL && mnew == -INFINITY) ? 1.f : tt_exp2((mrun[t] - mnew) * A.c);
           lrun[t] *= alpha;
 #pragma unroll
           for (int dt = 0; dt < D / 32; ++dt)
@@ -433,7 +447,8 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_partial(Args<T, D> A) {
             for (int j = 0; j < 16; ++j) o[t][dt][j] *= alpha;
           mrun[t] = mnew;
         }
-        const float mc = mrun[t] * A.c;
+        // (causal: a row may have no visible key yet in this piece; its probabilities are 0)
+        const float mc = (CAUSAL && mrun[t] == -INFINITY) ? 0.f : mrun[t] * A.c;
 #pragma unroll
         for (int j = 0; j < 16; ++j) sacc[t][j] = tt_exp2(fmaf(sacc[t][j], A.c, -mc));
 #pragma unroll
@@ -474,7 +489,7 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_partial(Args<T, D> A) {
       f32x16 sacc[TPW];
       qk(kf, sacc);
       frag pf[TPW][32 / KS];
-      softmax(sacc, kvalid, pf);
+      softmax(sacc, kvalid, ka + st * KC + kt * 32, pf);
       frag va[D / 32][32 / KS];
       vread(ring.v[st % NBUF], kt, va);
       pv(va, pf);
@@ -521,7 +536,8 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_partial(Args<T, D> A) {
             typedef PartT<T> PT;
             typedef PT pvec __attribute__((ext_vector_type(4)));
             PT* wp = A.ws_o + (slot * R + row) * D;
-            const float inv = 1.f / ltot;
+            // (causal: a row with no visible key in this piece leaves an empty partial)
+            const float inv = (CAUSAL && ltot == 0.f) ? 0.f : 1.f / ltot;
 #pragma unroll
             for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -675,7 +691,7 @@ __global__ __launch_bounds__(CB_THREADS) void attn_combine(Args<T, D> A) {
 constexpr int MIN_KEYS_PER_WG = TT_AT_MIN_KEYS;
 constexpr int AT_TARGET_WG = 256;
 
-template <typename T, int D>
+template <typename T, int D, bool CAUSAL>
 int launch(const void* q, const void* kb, const void* vb, const void* kc, const void* vc,
            const int32_t* cs, const int32_t* cl, void* out, int B, int S, int Hq, int Hkv,
            int64_t ctx_rows, int max_prefix, float scale, void* ws, size_t* ws_bytes,
@@ -700,7 +716,7 @@ int launch(const void* q, const void* kb, const void* vb, const void* kc, const 
   a.ws_ml = (float2*)((char*)ws + o_bytes);
   a.B = B; a.S = S; a.Hq = Hq; a.Hkv = Hkv; a.ctx_rows = ctx_rows; a.W = W;
   a.c = scale * LOG2E;
-  hipLaunchKernelGGL((attn_partial<T, D>), dim3(W), dim3(AT_THREADS), 0, stream, a);
+  hipLaunchKernelGGL((attn_partial<T, D, CAUSAL>), dim3(W), dim3(AT_THREADS), 0, stream, a);
   if (tt_launch_status() != TT_OK) return TT_ERR_HIP;
   if (W > 1) {
     // slot groups per row: enough to cover a unit's partials (about W / U + 1) in one batch
@@ -718,13 +734,12 @@ int launch(const void* q, const void* kb, const void* vb, const void* kc, const 
   return TT_OK;
 }
 
-}  // namespace
 
-extern "C" int tt_block_attn(const void* q, const void* k_blk, const void* v_blk, const void* k_ctx,
-                             const void* v_ctx, const int32_t* ctx_start, const int32_t* ctx_len,
-                             void* out, int B, int S, int Hq, int Hkv, int D, int64_t ctx_rows,
-                             int max_prefix, float softmax_scale, int dtype, void* workspace,
-                             size_t* workspace_bytes, void* stream) {
+// Host checks shared by the two attention entry points; TT_OK to proceed.
+int attn_check(const void* q, const void* k_blk, const void* v_blk, const void* k_ctx, const void* v_ctx,
+               const int32_t* ctx_start, const int32_t* ctx_len, const void* out, int B, int S, int Hq,
+               int Hkv, int D, int64_t ctx_rows, int max_prefix, float softmax_scale, int dtype,
+               const size_t* workspace_bytes) {
   if (!q || !k_blk || !v_blk || !ctx_start || !ctx_len || !out || !workspace_bytes) return TT_ERR_ARG;
   if (B <= 0 || S <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0) return TT_ERR_ARG;
   if (Hq % Hkv != 0 || ctx_rows < 0 || max_prefix < 0) return TT_ERR_ARG;
@@ -735,11 +750,78 @@ extern "C" int tt_block_attn(const void* q, const void* k_blk, const void* v_blk
   if ((int64_t)S * (Hq / Hkv) > MAX_ROWS) return TT_ERR_UNSUPPORTED;
   if (B > AT_MAX_B) return TT_ERR_UNSUPPORTED;
   if ((int64_t)B * Hkv * ((int64_t)max_prefix + S) >= ((int64_t)1 << 31)) return TT_ERR_UNSUPPORTED;
-  hipStream_t s = (hipStream_t)stream;
+  return TT_OK;
+}
+
+template <bool CAUSAL>
+int attn_dispatch(const void* q, const void* k_blk, const void* v_blk, const void* k_ctx, const void* v_ctx,
+                  const int32_t* ctx_start, const int32_t* ctx_len, void* out, int B, int S, int Hq, int Hkv,
+                  int D, int64_t ctx_rows, int max_prefix, float softmax_scale, int dtype, void* workspace,
+                  size_t* workspace_bytes, hipStream_t s) {
   if (dtype == TT_BF16) {
-    if (D == 128) return launch<bf16, 128>(q, k_blk, v_blk, k_ctx, v_ctx, ctx_start, ctx_len, out, B, S, Hq, Hkv, ctx_rows, max_prefix, softmax_scale, workspace, workspace_bytes, s);
-    return launch<bf16, 64>(q, k_blk, v_blk, k_ctx, v_ctx, ctx_start, ctx_len, out, B, S, Hq, Hkv, ctx_rows, max_prefix, softmax_scale, workspace, workspace_bytes, s);
+    if (D == 128) return launch<bf16, 128, CAUSAL>(q, k_blk, v_blk, k_ctx, v_ctx, ctx_start, ctx_len, out, B, S, Hq, Hkv, ctx_rows, max_prefix, softmax_scale, workspace, workspace_bytes, s);
+    return launch<bf16, 64, CAUSAL>(q, k_blk, v_blk, k_ctx, v_ctx, ctx_start, ctx_len, out, B, S, Hq, Hkv, ctx_rows, max_prefix, softmax_scale, workspace, workspace_bytes, s);
   }
-  if (D == 128) return launch<float, 128>(q, k_blk, v_blk, k_ctx, v_ctx, ctx_start, ctx_len, out, B, S, Hq, Hkv, ctx_rows, max_prefix, softmax_scale, workspace, workspace_bytes, s);
-  return launch<float, 64>(q, k_blk, v_blk, k_ctx, v_ctx, ctx_start, ctx_len, out, B, S, Hq, Hkv, ctx_rows, max_prefix, softmax_scale, workspace, workspace_bytes, s);
+  if (D == 128) return launch<float, 128, CAUSAL>(q, k_blk, v_blk, k_ctx, v_ctx, ctx_start, ctx_len, out, B, S, Hq, Hkv, ctx_rows, max_prefix, softmax_scale, workspace, workspace_bytes, s);
+  return launch<float, 64, CAUSAL>(q, k_blk, v_blk, k_ctx, v_ctx, ctx_start, ctx_len, out, B, S, Hq, Hkv, ctx_rows, max_prefix, softmax_scale, workspace, workspace_bytes, s);
+}
+
+// Appends the block's K/V rows to the cache and advances ctx_len: one workgroup per sequence b,
+// 16-byte copies; every thread reads ctx_len[b] before the barrier, thread 0 updates it after.
+constexpr int AP_THREADS = 256;
+__global__ __launch_bounds__(AP_THREADS) void kv_append(const unsigned char* __restrict__ k_new,
+                                                        const unsigned char* __restrict__ v_new,
+                                                        unsigned char* __restrict__ k_ctx,
+                                                        unsigned char* __restrict__ v_ctx,
+                                                        const int32_t* __restrict__ ctx_start,
+                                                        int32_t* __restrict__ ctx_len, int S, int Hkv,
+                                                        int row_bytes, int64_t ctx_rows) {
+  const int b = blockIdx.x;
+  const int64_t r0 = (int64_t)ctx_start[b] + ctx_len[b];  // first new cache row of sequence b
+  const int gpr = row_bytes / 16;                          // 16-byte granules per row
+  const int n = S * Hkv * gpr;
+  for (int x = threadIdx.x; x < n; x += AP_THREADS) {
+    const int gr = x % gpr, sg = x / gpr;
+    const int g = sg % Hkv, s = sg / Hkv;
+    const size_t src = (((size_t)b * S + s) * Hkv + g) * row_bytes + 16 * gr;
+    const size_t dst = ((size_t)g * ctx_rows + r0 + s) * row_bytes + 16 * gr;
+    *reinterpret_cast<u32x4*>(k_ctx + dst) = *reinterpret_cast<const u32x4*>(k_new + src);
+    *reinterpret_cast<u32x4*>(v_ctx + dst) = *reinterpret_cast<const u32x4*>(v_new + src);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) ctx_len[b] = ctx_len[b] + S;
+}
+
+}  // namespace
+
+extern "C" int tt_block_attn(const void* q, const void* k_blk, const void* v_blk, const void* k_ctx,
+                             const void* v_ctx, const int32_t* ctx_start, const int32_t* ctx_len,
+                             void* out, int B, int S, int Hq, int Hkv, int D, int64_t ctx_rows,
+                             int max_prefix, float softmax_scale, int dtype, void* workspace,
+                             size_t* workspace_bytes, void* stream) {
+  const int st = attn_check(q, k_blk, v_blk, k_ctx, v_ctx, ctx_start, ctx_len, out, B, S, Hq, Hkv, D, ctx_rows,
+                            max_prefix, softmax_scale, dtype, workspace_bytes);
+  if (st != TT_OK) return st;
+  return attn_dispatch<false>(q, k_blk, v_blk, k_ctx, v_ctx, ctx_start, ctx_len, out, B, S, Hq, Hkv, D, ctx_rows,
+                              max_prefix, softmax_scale, dtype, workspace, workspace_bytes, (hipStream_t)stream);
+}
+
+extern "C" int tt_context_extend(const void* q, const void* k_new, const void* v_new, void* k_ctx, void* v_ctx,
+                                 const int32_t* ctx_start, int32_t* ctx_len, void* out, int B, int S, int Hq,
+                                 int Hkv, int D, int64_t ctx_rows, int max_prefix, float softmax_scale, int dtype,
+                                 void* workspace, size_t* workspace_bytes, void* stream) {
+  if (!k_ctx || !v_ctx) return TT_ERR_ARG;  // the new rows are appended to the cache
+  int st = attn_check(q, k_new, v_new, k_ctx, v_ctx, ctx_start, ctx_len, out, B, S, Hq, Hkv, D, ctx_rows,
+                      max_prefix, softmax_scale, dtype, workspace_bytes);
+  if (st != TT_OK) return st;
+  if ((int64_t)max_prefix + S > ctx_rows) return TT_ERR_ARG;  // no room for any append
+  hipStream_t s = (hipStream_t)stream;
+  st = attn_dispatch<true>(q, k_new, v_new, k_ctx, v_ctx, ctx_start, ctx_len, out, B, S, Hq, Hkv, D, ctx_rows,
+                           max_prefix, softmax_scale, dtype, workspace, workspace_bytes, s);
+  if (st != TT_OK || workspace == nullptr) return st;  // an error, or a size query
+  const int row_bytes = D * (dtype == TT_BF16 ? 2 : 4);
+  hipLaunchKernelGGL(kv_append, dim3(B), dim3(AP_THREADS), 0, s, (const unsigned char*)k_new,
+                     (const unsigned char*)v_new, (unsigned char*)k_ctx, (unsigned char*)v_ctx, ctx_start, ctx_len,
+                     S, Hkv, row_bytes, ctx_rows);
+  return tt_launch_status();
 }

@@ -77,6 +77,36 @@ int tt_block_attn(const void* q, const void* k_blk, const void* v_blk,
                   void* workspace, size_t* workspace_bytes, void* stream);
 
 /*
+ * tt_context_extend — the context tower's attention step over a newly committed block, then the
+ * append of its keys/values to the cache ("Nemotron-Labs-TwoTower" wiki page, section
+ * "Block-wise generation": once a block is clean it is committed and the context tower processes
+ * the committed tokens causally to update its caches; the context tower's attention is causal).
+ *
+ * For every sequence b, committed position s and query head h (kv head g = h / (Hq/Hkv)):
+ *   keys   = [ k_ctx[g][ctx_start[b] .. ctx_start[b]+ctx_len[b]) ; k_new[b][0..s][g] ]
+ *   values = the same rows of v_ctx / v_new
+ *   out[b][s][h] = softmax(softmax_scale * keys . q[b][s][h]) . values
+ * i.e. tt_block_attn with the block made causal (new row j visible to positions s >= j only).
+ * Then, after the attention has read the cache: for j < S, cache row ctx_start[b]+ctx_len[b]+j
+ * of kv head g receives k_new[b][j][g] (and v_new likewise), and ctx_len[b] += S.
+ *
+ * Layouts as tt_block_attn (k_new, v_new in the place of k_blk, v_blk); k_ctx, v_ctx and
+ * ctx_len are updated in place. Caller's contract (not checked): ctx_len[b] <= max_prefix, and
+ * the S rows after each sequence's cached rows are inside [0, ctx_rows) and belong to it (no
+ * other sequence's rows there). Sizes, dtypes and limits as tt_block_attn.
+ * Errors: those of tt_block_attn; TT_ERR_ARG also for a null k_ctx / v_ctx, and when
+ *   max_prefix + S > ctx_rows (no room to append).
+ * Workspace: as tt_block_attn for the same arguments.
+ */
+int tt_context_extend(const void* q, const void* k_new, const void* v_new,
+                      void* k_ctx, void* v_ctx,
+                      const int32_t* ctx_start, int32_t* ctx_len,
+                      void* out,
+                      int B, int S, int Hq, int Hkv, int D, int64_t ctx_rows, int max_prefix,
+                      float softmax_scale, int dtype,
+                      void* workspace, size_t* workspace_bytes, void* stream);
+
+/*
  * tt_lmhead_logits — vocabulary logits of every block position ("Nemotron-Labs-TwoTower" wiki
  * page, section "Block-wise generation": each step predicts all masked positions in parallel).
  *

@@ -24,7 +24,10 @@ Readings where the pages are silent (each also listed in the design notes):
   * the completion floor commits the k = ceil(n_masked / (T - step)) most confident
     masked positions when fewer than k clear gamma (ties: lower position first);
   * argmax ties go to the lowest vocabulary id;
-  * the LM head is a bias-free product hidden . W^T with fp32 logits.
+  * the LM head is a bias-free product hidden . W^T with fp32 logits;
+  * the context tower's step over a committed block: its new keys/values arrive as inputs
+    (synthetic projections), attention is causal inside the block, and the new rows are
+    appended right after each sequence's cached rows.
 
 Parity pins: every function here is pinned by the ``-m "not gpu"`` tests
 (brute force, closed forms, library special cases, invariants and a hand-worked
@@ -113,6 +116,60 @@ def block_attention(inp: dict, dtype: str, rows: Optional[Iterable[Tuple[int, in
             out[b, :, g * G:(g + 1) * G, :] = o.reshape(S, G, D)
             probs[(b, g)] = p.reshape(S, G, -1)
     return (out, probs) if return_probs else out
+
+
+def context_extend(inp: dict, dtype: str, rows: Optional[Iterable[Tuple[int, int, int]]] = None):
+    """The context tower's step over a newly committed block ([wiki] "Block-wise generation": once
+    a block is clean it is committed and the context tower processes the committed tokens
+    causally to update its caches; [wiki] "Architecture" and [overview]: the context tower uses
+    causal attention).
+
+    inp: like block_attention's, with k_blk / v_blk holding the context tower's keys and values
+    of the S committed tokens (k_new / v_new). For sequence b, position s, query head h, kv head
+    g = h // (Hq/Hkv):
+        K = [K_ctx[g, start_b : start_b + len_b] ; K_new[b, 0 .. s, g]]   (V likewise)
+        o = softmax(scale * K q_{b,s,h}) V
+    i.e. the prefix is visible to every new position and new row j only to positions s >= j.
+    Then the new rows are appended: cache rows start_b + len_b + j (j < S) of kv head g get
+    K_new[b, j, g] / V_new[b, j, g], and len_b grows by S.
+
+    rows: optional iterable of (b, s, h): returns {(b, s, h): o} only (no cache update).
+    Otherwise returns (o float64 [B][S][Hq][D], k_ctx', v_ctx' (copies, same dtype as given),
+    ctx_len' int32 [B])."""
+    q = inp["q"]
+    B, S, Hq, D = q.shape
+    Hkv = inp["k_blk"].shape[2]
+    G = Hq // Hkv
+    scale = float(inp["scale"])
+    starts = np.asarray(inp["ctx_start"], dtype=np.int64)
+    lens = np.asarray(inp["ctx_len"], dtype=np.int64)
+
+    def attend_one(b: int, s: int, h: int) -> np.ndarray:
+        g = h // G
+        a, n = int(starts[b]), int(lens[b])
+        K = np.concatenate([decode(inp["k_ctx"][g, a:a + n], dtype),
+                            decode(inp["k_blk"][b, :s + 1, g], dtype)], axis=0)
+        Vv = np.concatenate([decode(inp["v_ctx"][g, a:a + n], dtype),
+                             decode(inp["v_blk"][b, :s + 1, g], dtype)], axis=0)
+        z = scale * (K @ decode(q[b, s, h], dtype))
+        e = np.exp(z - z.max())
+        return (e / e.sum()) @ Vv
+
+    if rows is not None:
+        return {(int(b), int(s), int(h)): attend_one(int(b), int(s), int(h)) for (b, s, h) in rows}
+    out = np.zeros((B, S, Hq, D), dtype=np.float64)
+    for b in range(B):
+        for s in range(S):
+            for h in range(Hq):
+                out[b, s, h] = attend_one(b, s, h)
+    k_ctx = np.array(inp["k_ctx"], copy=True)
+    v_ctx = np.array(inp["v_ctx"], copy=True)
+    for b in range(B):
+        r0 = int(starts[b] + lens[b])
+        for j in range(S):
+            k_ctx[:, r0 + j] = inp["k_blk"][b, j]
+            v_ctx[:, r0 + j] = inp["v_blk"][b, j]
+    return out, k_ctx, v_ctx, (lens + S).astype(np.int32)
 
 
 # ----------------------------------------------------------------------------- LM head

@@ -32,6 +32,7 @@ import numpy as np
 T_Q, T_KBLK, T_VBLK, T_KCTX, T_VCTX = 1, 2, 3, 4, 5
 T_HIDDEN, T_W, T_SPIKE_TOK, T_SPIKE_VAL, T_LOGIT_NOISE = 6, 7, 8, 9, 10
 T_LENS, T_MASK_INIT, T_MASK_TOK, T_PERM = 11, 12, 13, 14
+T_SPARE = 15  # filler of the cache rows reserved for appends
 
 
 @dataclass
@@ -155,6 +156,32 @@ def attn_inputs(wl: Workload, layer: int = 0) -> dict:
         ctx_len=wl.ctx_len,
         scale=float(1.0 / np.sqrt(wl.D)),
     )
+
+
+def context_inputs(wl: Workload, layer: int = 0) -> dict:
+    """Inputs of the context tower's step over a committed block: q / k_blk / v_blk as in
+    attn_inputs (here the new tokens' queries, keys and values) and a cache laid out with room
+    for S more rows per sequence: sequence b owns rows [start_b, start_b + prefix_b + S), the
+    first prefix_b of them cached, the last S filled with N(0,1) filler to be overwritten."""
+    B, S, Hq, Hkv, D = wl.B, wl.S, wl.Hq, wl.Hkv, wl.D
+    p = np.asarray(wl.prefixes, dtype=np.int64)
+    cap = p + S
+    start = (np.cumsum(cap) - cap).astype(np.int32)
+    R = int(cap.sum())
+    base = attn_inputs(wl, layer)
+    kc = np.empty((Hkv, R, D), dtype=base["k_ctx"].dtype)
+    vc = np.empty_like(kc)
+    fill_k = _store(_normal(rng(wl.wid, T_SPARE, layer, 1), (Hkv, R, D)), wl.dtype)
+    fill_v = _store(_normal(rng(wl.wid, T_SPARE, layer, 2), (Hkv, R, D)), wl.dtype)
+    kc[:], vc[:] = fill_k, fill_v
+    src = 0
+    for b in range(B):
+        n = int(p[b])
+        kc[:, start[b]:start[b] + n] = base["k_ctx"][:, src:src + n]
+        vc[:, start[b]:start[b] + n] = base["v_ctx"][:, src:src + n]
+        src += n
+    return dict(q=base["q"], k_blk=base["k_blk"], v_blk=base["v_blk"], k_ctx=kc, v_ctx=vc,
+                ctx_start=start, ctx_len=p.astype(np.int32), scale=base["scale"])
 
 
 def lmhead_inputs(wl: Workload) -> dict:

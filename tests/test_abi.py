@@ -162,3 +162,30 @@ def test_fused_argument_errors(kw, code):
 
 def test_fused_bias_pair_accepted():
     assert _fu(bt=P, bv=P)[0] == 0
+
+
+def _ce(ws=None, nbytes=0, **kw):
+    a = dict(q=P, kn=P, vn=P, kc=P, vc=P, cs=P, cl=P, out=P, B=1, S=16, Hq=32, Hkv=2, D=128,
+             ctx_rows=2048 + 16, max_prefix=2048, scale=0.088, dtype=_lib.TT_BF16)
+    a.update(kw)
+    n = ctypes.c_size_t(nbytes)
+    st = _lib.load().tt_context_extend(a["q"], a["kn"], a["vn"], a["kc"], a["vc"], a["cs"], a["cl"], a["out"],
+                                       a["B"], a["S"], a["Hq"], a["Hkv"], a["D"], a["ctx_rows"], a["max_prefix"],
+                                       a["scale"], a["dtype"], ws, ctypes.byref(n), None)
+    return st, n.value
+
+
+def test_context_extend_workspace_matches_block_attention():
+    st, n = _ce()
+    st2, n2 = _attn(ctx_rows=2048 + 16)
+    assert st == 0 and st2 == 0 and n == n2 > 0
+    assert _ce(ws=P, nbytes=10)[0] == _lib.TT_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(kn=None), -1), (dict(kc=None, max_prefix=0), -1), (dict(vc=None, max_prefix=0), -1),
+    (dict(cl=None), -1), (dict(B=0), -1), (dict(Hq=33), -1), (dict(scale=float("nan")), -1),
+    (dict(ctx_rows=2048 + 15), -1), (dict(D=96), -2), (dict(S=17), -2), (dict(dtype=4), -2),
+])
+def test_context_extend_argument_errors(kw, code):
+    assert _ce(**kw)[0] == code
