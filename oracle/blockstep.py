@@ -200,22 +200,25 @@ def masked_softmax(row: np.ndarray, mask_id: int) -> np.ndarray:
     return e / e.sum()
 
 
-def reduce_row(row: np.ndarray, mask_id: int) -> Tuple[float, int]:
+def reduce_row(row: np.ndarray, mask_id: int, temperature: float = 1.0) -> Tuple[float, int]:
     """(confidence, prediction) of one position: the largest probability of the masked
     softmax and the lowest vocabulary id that attains it ([wiki] "Block-wise generation";
-    [blog] "Adaptive Step-wise Generation")."""
+    [blog] "Adaptive Step-wise Generation"). With a temperature (the model card's diffusion
+    example uses 0.1), the softmax is taken of logits / temperature; the prediction does not
+    change."""
     l = np.array(row, dtype=np.float64)
     l[mask_id] = -np.inf
     m = l.max()
     a = int(np.flatnonzero(l == m)[0])
-    s = float(np.exp(l - m).sum())
+    s = float(np.exp((l - m) / float(temperature)).sum())
     return 1.0 / s, a
 
 
 # ----------------------------------------------------------------------------- commit
 
 def commit_block(conf: Sequence[float], pred: Sequence[int], tokens: np.ndarray, mask_bits: int,
-                 S: int, step: int, T: int, gamma: float) -> Tuple[np.ndarray, int, int, List[int]]:
+                 S: int, step: int, T: int, gamma: float,
+                 kind: str = "confidence") -> Tuple[np.ndarray, int, int, List[int]]:
     """One step of confidence unmasking for one block ([wiki] "Block-wise generation":
     every masked position is predicted in parallel; predictions whose confidence clears
     gamma are committed, the rest stay masked; a floor makes the block finish within T
@@ -228,15 +231,27 @@ def commit_block(conf: Sequence[float], pred: Sequence[int], tokens: np.ndarray,
       if |C| < k: C = the k positions of Mk with the largest confidence (ties: lower i)
       for i in C: token_i = pred_i, clear bit i
       n_masked = |Mk| - |C|   (next step's timestep is n_masked / S)
+    kind "predict_noise" is the block-diffusion sampler the wiki page mentions beside it (every
+    masked position is predicted, then the lowest-confidence ones are re-masked as the noise
+    schedule dictates): with a linear schedule, target = floor(S (T - 1 - step) / T) positions
+    stay masked after the step, so C = the n_masked - target most confident masked positions
+    (ties: lower i), none if n_masked <= target; gamma is not used.
     Returns (tokens, mask_bits, n_masked, committed positions)."""
     tokens = np.array(tokens, dtype=np.int32, copy=True)
     Mk = [i for i in range(S) if (mask_bits >> i) & 1]
     if not Mk:
         return tokens, mask_bits, 0, []
-    C = [i for i in Mk if conf[i] >= gamma]
-    k = -(-len(Mk) // (T - step))
-    if len(C) < k:
+    if kind == "predict_noise":
+        target = (S * (T - 1 - step)) // T
+        k = max(len(Mk) - target, 0)
         C = sorted(Mk, key=lambda i: (-conf[i], i))[:k]
+    elif kind == "confidence":
+        C = [i for i in Mk if conf[i] >= gamma]
+        k = -(-len(Mk) // (T - step))
+        if len(C) < k:
+            C = sorted(Mk, key=lambda i: (-conf[i], i))[:k]
+    else:
+        raise ValueError(kind)
     for i in sorted(C):
         tokens[i] = pred[i]
         mask_bits &= ~(1 << i)
@@ -244,7 +259,8 @@ def commit_block(conf: Sequence[float], pred: Sequence[int], tokens: np.ndarray,
 
 
 def confidence_unmask(logits: np.ndarray, tokens: np.ndarray, mask_bits: np.ndarray, S: int,
-                      step: int, T: int, gamma: float, mask_id: int):
+                      step: int, T: int, gamma: float, mask_id: int, temperature: float = 1.0,
+                      kind: str = "confidence"):
     """The whole unmask call over B blocks: logits [B*S][V] (any float dtype, read as float64),
     tokens int32 [B][S], mask_bits uint64 [B]. Rows of positions that are not masked at the
     start of the step are not read and keep their tokens.
@@ -262,9 +278,9 @@ def confidence_unmask(logits: np.ndarray, tokens: np.ndarray, mask_bits: np.ndar
         bits = int(mask_bits[b])
         for i in range(S):
             if (bits >> i) & 1:
-                c, a = reduce_row(logits[b * S + i], mask_id)
+                c, a = reduce_row(logits[b * S + i], mask_id, temperature)
                 conf[b, i], pred[b, i] = c, a
-        t, nb, nm, C = commit_block(conf[b], pred[b], tokens[b], bits, S, step, T, gamma)
+        t, nb, nm, C = commit_block(conf[b], pred[b], tokens[b], bits, S, step, T, gamma, kind)
         tok_out[b], bits_out[b], n_masked[b] = t, np.uint64(nb), nm
         committed.append(C)
     return dict(tokens=tok_out, mask_bits=bits_out, n_masked=n_masked, conf=conf, pred=pred,
