@@ -16,7 +16,7 @@ from . import _lib
 from ._lib import TTError, TT_BF16, TT_F32
 
 __all__ = ["tt_block_attn", "tt_context_extend", "tt_lmhead_logits", "tt_confidence_unmask",
-           "tt_lmhead_unmask", "workspace_bytes", "TTError", "abi_version"]
+           "tt_unmask_sample", "tt_lmhead_unmask", "workspace_bytes", "TTError", "abi_version"]
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -74,12 +74,17 @@ def workspace_bytes(fn: str, **kw) -> int:
     elif fn == "tt_lmhead_unmask":
         one = ctypes.c_void_p(16)
         st = lib.tt_lmhead_unmask(one, one, None, None, one, one, one, None, None, kw["B"], kw["S"], kw["H"],
-                                  kw["V"], 0, 1, 0.5, kw.get("mask_id", 0), kw.get("dtype", TT_BF16), None,
-                                  ctypes.byref(n), None)
+                                  kw["V"], 0, 1, ctypes.byref(_sampler("confidence", 0.5, 1.0)),
+                                  kw.get("mask_id", 0), kw.get("dtype", TT_BF16), None, ctypes.byref(n), None)
     else:
         raise ValueError(fn)
     _check(st, fn)
     return n.value
+
+
+def _sampler(kind: str, gamma: float, temperature: float) -> "_lib.Sampler":
+    _need(kind in _lib.SAMPLER_KINDS, f"sampler kind is one of {sorted(_lib.SAMPLER_KINDS)}")
+    return _lib.Sampler(_lib.SAMPLER_KINDS[kind], float(gamma), float(temperature))
 
 
 def _workspace(nbytes: int, workspace: Optional[torch.Tensor], device) -> torch.Tensor:
@@ -197,6 +202,30 @@ def tt_confidence_unmask(logits: torch.Tensor, tokens: torch.Tensor, mask_bits: 
     _check(lib.tt_confidence_unmask(*args, _ptr(ws), ctypes.byref(n2), _stream(stream)), "tt_confidence_unmask")
 
 
+def tt_unmask_sample(logits: torch.Tensor, tokens: torch.Tensor, mask_bits: torch.Tensor,
+                     n_masked: torch.Tensor, step: int, num_steps: int, mask_id: int,
+                     sampler: str = "confidence", gamma: float = 0.8, temperature: float = 1.0,
+                     conf_out: Optional[torch.Tensor] = None, pred_out: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """One unmasking step with a chosen sampler ("confidence" or "predict_noise") and softmax
+    temperature, in place on tokens / mask_bits (see include/tt.h)."""
+    _need(tokens.dim() == 2 and tokens.dtype == torch.int32, "tokens int32 [B][S]")
+    B, S = tokens.shape
+    _need(logits.dtype == torch.float32 and logits.dim() == 2 and logits.shape[0] == B * S, "logits fp32 [B*S][V]")
+    V = logits.shape[1]
+    _unmask_io(B, S, tokens, mask_bits, n_masked, conf_out, pred_out)
+    _dev(logits, tokens, mask_bits, n_masked, conf_out, pred_out)
+    sm = _sampler(sampler, gamma, temperature)
+    lib = _lib.load()
+    n = ctypes.c_size_t(0)
+    args = [_ptr(logits), _ptr(tokens), _ptr(mask_bits), _ptr(n_masked), _ptr(conf_out), _ptr(pred_out),
+            B, S, V, int(step), int(num_steps), ctypes.byref(sm), int(mask_id)]
+    _check(lib.tt_unmask_sample(*args, None, ctypes.byref(n), None), "tt_unmask_sample")
+    ws = _workspace(n.value, workspace, logits.device)
+    n2 = ctypes.c_size_t(ws.numel() * ws.element_size())
+    _check(lib.tt_unmask_sample(*args, _ptr(ws), ctypes.byref(n2), _stream(stream)), "tt_unmask_sample")
+
+
 def _unmask_io(B: int, S: int, tokens, mask_bits, n_masked, conf_out, pred_out):
     _need(mask_bits.dtype in (torch.int64, torch.uint64) and mask_bits.numel() == B, "mask_bits 64-bit [B]")
     _need(n_masked.dtype == torch.int32 and n_masked.numel() == B, "n_masked int32 [B]")
@@ -210,11 +239,13 @@ def tt_lmhead_unmask(hidden: torch.Tensor, w: torch.Tensor, tokens: torch.Tensor
                      n_masked: torch.Tensor, step: int, num_steps: int, gamma: float, mask_id: int,
                      bias_tok: Optional[torch.Tensor] = None, bias_val: Optional[torch.Tensor] = None,
                      conf_out: Optional[torch.Tensor] = None, pred_out: Optional[torch.Tensor] = None,
-                     workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+                     workspace: Optional[torch.Tensor] = None, stream=None, sampler: str = "confidence",
+                     temperature: float = 1.0) -> None:
     """LM head + one confidence-unmasking step without materialising the logits (see
     include/tt.h). hidden bf16 [B*S][H], w bf16 [V][H]; tokens int32 [B][S] and mask_bits
     (64-bit) [B] are updated in place; optional one-entry-per-row logit bias bias_tok int32 /
-    bias_val fp32 [B*S]."""
+    bias_val fp32 [B*S]; sampler "confidence" (threshold gamma) or "predict_noise", softmax
+    temperature."""
     _need(tokens.dim() == 2 and tokens.dtype == torch.int32, "tokens int32 [B][S]")
     B, S = tokens.shape
     _need(hidden.dim() == 2 and w.dim() == 2 and hidden.shape[1] == w.shape[1], "hidden [M][H], w [V][H]")
@@ -227,10 +258,11 @@ def tt_lmhead_unmask(hidden: torch.Tensor, w: torch.Tensor, tokens: torch.Tensor
     _unmask_io(B, S, tokens, mask_bits, n_masked, conf_out, pred_out)
     _dev(hidden, w, tokens, mask_bits, n_masked, bias_tok, bias_val, conf_out, pred_out)
     H, V = hidden.shape[1], w.shape[0]
+    sm = _sampler(sampler, gamma, temperature)
     lib = _lib.load()
     n = ctypes.c_size_t(0)
     args = [_ptr(hidden), _ptr(w), _ptr(bias_tok), _ptr(bias_val), _ptr(tokens), _ptr(mask_bits), _ptr(n_masked),
-            _ptr(conf_out), _ptr(pred_out), B, S, H, V, int(step), int(num_steps), float(gamma), int(mask_id),
+            _ptr(conf_out), _ptr(pred_out), B, S, H, V, int(step), int(num_steps), ctypes.byref(sm), int(mask_id),
             _dtype(hidden)]
     _check(lib.tt_lmhead_unmask(*args, None, ctypes.byref(n), None), "tt_lmhead_unmask")
     ws = _workspace(n.value, workspace, hidden.device)

@@ -22,7 +22,15 @@ TT_OK, TT_ERR_ARG, TT_ERR_UNSUPPORTED, TT_ERR_WORKSPACE, TT_ERR_HIP = 0, -1, -2,
 
 # every symbol include/tt.h declares
 EXPORTS = ("tt_block_attn", "tt_context_extend", "tt_lmhead_logits", "tt_confidence_unmask",
-           "tt_lmhead_unmask", "tt_status_string", "tt_abi_version")
+           "tt_unmask_sample", "tt_lmhead_unmask", "tt_status_string", "tt_abi_version")
+
+TT_SAMPLER_CONFIDENCE, TT_SAMPLER_PREDICT_NOISE = 0, 1
+SAMPLER_KINDS = {"confidence": TT_SAMPLER_CONFIDENCE, "predict_noise": TT_SAMPLER_PREDICT_NOISE}
+
+
+class Sampler(ctypes.Structure):
+    """struct tt_sampler of include/tt.h."""
+    _fields_ = [("kind", ctypes.c_int), ("gamma", ctypes.c_float), ("temperature", ctypes.c_float)]
 
 _lib = None
 
@@ -64,7 +72,10 @@ def load() -> ctypes.CDLL:
     lib.tt_lmhead_logits.restype = i
     lib.tt_confidence_unmask.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f32, i, vp, sz, vp]
     lib.tt_confidence_unmask.restype = i
-    lib.tt_lmhead_unmask.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f32, i, i, vp, sz, vp]
+    smp = ctypes.POINTER(Sampler)
+    lib.tt_unmask_sample.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, smp, i, vp, sz, vp]
+    lib.tt_unmask_sample.restype = i
+    lib.tt_lmhead_unmask.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, smp, i, i, vp, sz, vp]
     lib.tt_lmhead_unmask.restype = i
     lib.tt_status_string.argtypes = [i]
     lib.tt_status_string.restype = ctypes.c_char_p

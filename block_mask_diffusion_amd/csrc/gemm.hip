@@ -277,7 +277,7 @@ __global__ __launch_bounds__(LM_THREADS, 1) __attribute__((amdgpu_waves_per_eu(1
           for (int q = 0; q < w2; ++q) mx[q] = fmaxf(mx[q], mx[q + w2]);
         const float rm = fmaxf(mx[0], tt_swap_halves(mx[0]));
         const bool empty = (rm == -INFINITY);
-        const float mb = empty ? 0.f : rm * TT_LOG2E;
+        const float mb = empty ? 0.f : rm * red.c;
         int kf = 64;  // first k (lowest id) of this lane holding the maximum; 64 = none
 #pragma unroll
         for (int k = 63; k >= 0; --k) {
@@ -291,7 +291,7 @@ __global__ __launch_bounds__(LM_THREADS, 1) __attribute__((amdgpu_waves_per_eu(1
         for (int q = 0; q < 8; ++q) {
           sm[q] = 0.f;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) sm[q] += tt_exp2(fmaf(v[8 * q + e], TT_LOG2E, -mb));
+          for (int e = 0; e < 8; ++e) sm[q] += tt_exp2(fmaf(v[8 * q + e], red.c, -mb));
         }
 #pragma unroll
         for (int w2 = 4; w2 >= 1; w2 >>= 1)

@@ -410,7 +410,7 @@ __global__ __launch_bounds__(LM_THREADS) void lmhead_lds_kernel(const bf16* __re
           for (int vt = 0; vt < VT; ++vt) v[vt] = acc[mt][vt][j];
           float rm, rs;
           int ra;
-          tt_row_reduce<VT, NV>(v, cb, NV, col, rm, ra, rs);
+          tt_row_reduce<VT, NV>(v, cb, NV, col, red.c, rm, ra, rs);
           emit(m0 + mt * MT + SH::row(lane, j), rm, ra, rs);
         }
     } else {
@@ -428,7 +428,7 @@ __global__ __launch_bounds__(LM_THREADS) void lmhead_lds_kernel(const bf16* __re
             v[vt] = tt_red_logit(acc[mt][vt][j], cb + vt * NV + col, V, btok, bval, red.mask_id);
           float rm, rs;
           int ra;
-          tt_row_reduce<VT, NV>(v, cb, NV, col, rm, ra, rs);
+          tt_row_reduce<VT, NV>(v, cb, NV, col, red.c, rm, ra, rs);
           emit(m, rm, ra, rs);
         }
     }

@@ -4,8 +4,9 @@
 
 #include "common.h"
 
-// (max, lowest argmax, sum of exp(l - max)) of a set of logits of one row; m = -inf and
-// a = INT32_MAX for an empty set.
+// (max, lowest argmax, sum of exp((l - max) / temperature)) of a set of logits of one row; m =
+// -inf and a = INT32_MAX for an empty set. The sums of one call share the scale c =
+// log2(e) / temperature: s = sum exp2((l - m) c).
 struct alignas(16) TtPartial {
   float m;
   float s;
@@ -15,12 +16,12 @@ struct alignas(16) TtPartial {
 
 constexpr float TT_LOG2E = 1.4426950408889634f;
 
-// Merge (m2, a2, s2) into (m, a, s); ties of the max keep the lower index.
-__device__ __forceinline__ void tt_merge(float& m, int& a, float& s, float m2, int a2, float s2) {
+// Merge (m2, a2, s2) into (m, a, s) at scale c; ties of the max keep the lower index.
+__device__ __forceinline__ void tt_merge(float& m, int& a, float& s, float m2, int a2, float s2, float c) {
   const float M = fmaxf(m, m2);
   if (M == -INFINITY) return;  // both empty
-  const float t1 = (m == -INFINITY) ? 0.f : s * tt_exp2((m - M) * TT_LOG2E);
-  const float t2 = (m2 == -INFINITY) ? 0.f : s2 * tt_exp2((m2 - M) * TT_LOG2E);
+  const float t1 = (m == -INFINITY) ? 0.f : s * tt_exp2((m - M) * c);
+  const float t2 = (m2 == -INFINITY) ? 0.f : s2 * tt_exp2((m2 - M) * c);
   const int an = (m2 > m) ? a2 : ((m > m2) ? a : min(a, a2));
   m = M;
   a = an;
@@ -38,6 +39,7 @@ struct TtRedArgs {
   // can skip the other rows do; NULL = every row)
   const uint64_t* mask_bits;
   int S, B;
+  float c;                  // log2(e) / temperature
 };
 
 // Cross-lane partner values for a butterfly over groups of up to 32 consecutive lanes, all on
@@ -101,22 +103,23 @@ __device__ __forceinline__ int tt_group_min(int x) {
 // Row reduction across an aligned group of NL consecutive lanes (16 or 32) that hold the same
 // row: lane `col` of the group brings the K logits of vocabulary ids cb + k * stride + col
 // (stride >= NL; -inf for excluded entries). Returns, on every lane of the group, the row's
-// (max, lowest id attaining it, sum exp(l - max)); an all -inf row gives (-inf, INT32_MAX, 0).
+// (max, lowest id attaining it, sum exp2((l - max) c)); an all -inf row gives (-inf, INT32_MAX,
+// 0).
 template <int K, int NL>
-__device__ __forceinline__ void tt_row_reduce(const float (&v)[K], int cb, int stride, int col, float& M,
-                                              int& A, float& S) {
+__device__ __forceinline__ void tt_row_reduce(const float (&v)[K], int cb, int stride, int col, float c,
+                                              float& M, int& A, float& S) {
   float m = v[0];
 #pragma unroll
   for (int k = 1; k < K; ++k) m = fmaxf(m, v[k]);
   m = tt_group_max<NL>(m);
   const bool empty = (m == -INFINITY);
-  const float mb = empty ? 0.f : m * TT_LOG2E;
+  const float mb = empty ? 0.f : m * c;
   int key = INT32_MAX;  // k * NL + col of this lane's first maximum: ordered like the vocabulary id
 #pragma unroll
   for (int k = K - 1; k >= 0; --k) key = (v[k] == m) ? k * NL + col : key;
   float s = 0.f;
 #pragma unroll
-  for (int k = 0; k < K; ++k) s += tt_exp2(fmaf(v[k], TT_LOG2E, -mb));
+  for (int k = 0; k < K; ++k) s += tt_exp2(fmaf(v[k], c, -mb));
   key = tt_group_min<NL>(key);
   s = tt_group_sum<NL>(s);
   M = m;

@@ -25,22 +25,22 @@ constexpr int UM_THREADS = 256;
 #endif
 constexpr int UM_PER_THREAD = TT_UM_PER_THREAD;
 constexpr int UM_CHUNK = UM_THREADS * UM_PER_THREAD;  // vocabulary entries per workgroup
-constexpr float LOG2E = TT_LOG2E;
 typedef TtPartial Partial;
 
-__device__ __forceinline__ void merge(float& m, int& a, float& s, float m2, int a2, float s2) {
-  tt_merge(m, a, s, m2, a2, s2);
+// c = log2(e) / temperature: every record's sum is sum exp2((l - m) c)
+__device__ __forceinline__ void merge(float& m, int& a, float& s, float m2, int a2, float s2, float c) {
+  tt_merge(m, a, s, m2, a2, s2, c);
 }
 
 // Merges the records of the workgroup's UM_THREADS threads in a fixed order (butterfly inside each
 // wave, then the waves in increasing order) and stores the result to *out from thread 0.
-__device__ __forceinline__ void wg_merge_store(float m, int a, float s, Partial* out) {
+__device__ __forceinline__ void wg_merge_store(float m, int a, float s, Partial* out, float c) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
     float m2 = tt_shfl_xor(m, off);
     int a2 = tt_shfl_xor(a, off);
     float s2 = tt_shfl_xor(s, off);
-    merge(m, a, s, m2, a2, s2);
+    merge(m, a, s, m2, a2, s2, c);
   }
   __shared__ float sm[UM_THREADS / TT_WAVE], ss[UM_THREADS / TT_WAVE];
   __shared__ int sa[UM_THREADS / TT_WAVE];
@@ -52,7 +52,7 @@ __device__ __forceinline__ void wg_merge_store(float m, int a, float s, Partial*
   }
   __syncthreads();
   if (t == 0) {
-    for (int k = 1; k < UM_THREADS / TT_WAVE; ++k) merge(m, a, s, sm[k], sa[k], ss[k]);
+    for (int k = 1; k < UM_THREADS / TT_WAVE; ++k) merge(m, a, s, sm[k], sa[k], ss[k], c);
     Partial p;
     p.m = m;
     p.s = s;
@@ -66,7 +66,7 @@ template <bool VEC4>
 __global__ __launch_bounds__(UM_THREADS) void unmask_partial(const float* __restrict__ logits,
                                                              const uint64_t* __restrict__ mask_bits,
                                                              Partial* __restrict__ ws, int S, int V,
-                                                             int nchunk, int mask_id) {
+                                                             int nchunk, int mask_id, float cs) {
   const int r = blockIdx.x / nchunk;
   const int c = blockIdx.x - r * nchunk;
   const int b = r / S, i = r - b * S;
@@ -116,11 +116,11 @@ __global__ __launch_bounds__(UM_THREADS) void unmask_partial(const float* __rest
   }
   float s = 0.f;
   if (m != -INFINITY) {
-    const float mb = m * LOG2E;
+    const float mb = m * cs;
 #pragma unroll
-    for (int k = 0; k < UM_PER_THREAD; ++k) s += tt_exp2(fmaf(x[k], LOG2E, -mb));
+    for (int k = 0; k < UM_PER_THREAD; ++k) s += tt_exp2(fmaf(x[k], cs, -mb));
   }
-  wg_merge_store(m, a, s, ws + (size_t)r * nchunk + c);
+  wg_merge_store(m, a, s, ws + (size_t)r * nchunk + c, cs);
 }
 
 // One workgroup per (block, position) of the fused path: the row's nparts records (one per column
@@ -130,7 +130,7 @@ constexpr int RM_BATCH = 4;
 __global__ __launch_bounds__(UM_THREADS) void unmask_rowmerge(const Partial* __restrict__ parts,
                                                               const uint64_t* __restrict__ mask_bits,
                                                               Partial* __restrict__ rowres, int S,
-                                                              int nparts) {
+                                                              int nparts, float cs) {
   const int r = blockIdx.x;
   const int b = r / S, i = r - b * S;
   if (!((mask_bits[b] >> i) & 1ull)) return;
@@ -146,9 +146,9 @@ __global__ __launch_bounds__(UM_THREADS) void unmask_rowmerge(const Partial* __r
       else x[k] = Partial{-INFINITY, 0.f, INT32_MAX, 0};
     }
 #pragma unroll
-    for (int k = 0; k < RM_BATCH; ++k) merge(m, a, s, x[k].m, x[k].a, x[k].s);
+    for (int k = 0; k < RM_BATCH; ++k) merge(m, a, s, x[k].m, x[k].a, x[k].s, cs);
   }
-  wg_merge_store(m, a, s, rowres + r);
+  wg_merge_store(m, a, s, rowres + r, cs);
 }
 
 constexpr int CM_THREADS = 256;
@@ -158,7 +158,9 @@ constexpr int CM_BATCH = 8;                 // partial loads issued before mergi
 // One workgroup per block. Thread (stripe q, row i) merges the partials c = q, q+4, q+8, ... of
 // row i, issuing a batch of loads before merging them in increasing c; wave 0 then merges the four
 // stripes in the order q = 0..3 (a fixed order: bitwise reproducible), so lane i holds row i's
-// confidence and prediction, and applies the commit rule for the block.
+// confidence and prediction, and applies the commit rule for the block:
+//   kind TT_SAMPLER_CONFIDENCE: conf >= gamma, topped up to the completion floor;
+//   kind TT_SAMPLER_PREDICT_NOISE: the n_masked - floor(S (T-1-step) / T) most confident.
 __global__ __launch_bounds__(CM_THREADS) void unmask_commit(const Partial* __restrict__ ws,
                                                            int32_t* __restrict__ tokens,
                                                            uint64_t* __restrict__ mask_bits,
@@ -166,7 +168,7 @@ __global__ __launch_bounds__(CM_THREADS) void unmask_commit(const Partial* __res
                                                            float* __restrict__ conf_out,
                                                            int32_t* __restrict__ pred_out, int S,
                                                            int nchunk, int step, int num_steps,
-                                                           float gamma) {
+                                                           int kind, float gamma, float cs) {
   __shared__ float pm[CM_Q][TT_WAVE], ps[CM_Q][TT_WAVE];
   __shared__ int pa[CM_Q][TT_WAVE];
   const int b = blockIdx.x;
@@ -186,7 +188,7 @@ __global__ __launch_bounds__(CM_THREADS) void unmask_commit(const Partial* __res
         else x[k] = Partial{-INFINITY, 0.f, INT32_MAX, 0};
       }
 #pragma unroll
-      for (int k = 0; k < CM_BATCH; ++k) merge(m, a, s, x[k].m, x[k].a, x[k].s);
+      for (int k = 0; k < CM_BATCH; ++k) merge(m, a, s, x[k].m, x[k].a, x[k].s, cs);
     }
   }
   pm[q][i] = m;
@@ -195,7 +197,7 @@ __global__ __launch_bounds__(CM_THREADS) void unmask_commit(const Partial* __res
   __syncthreads();
   if (q != 0) return;
 #pragma unroll
-  for (int k = 1; k < CM_Q; ++k) merge(m, a, s, pm[k][i], pa[k][i], ps[k][i]);
+  for (int k = 1; k < CM_Q; ++k) merge(m, a, s, pm[k][i], pa[k][i], ps[k][i], cs);
   float conf = -1.f;
   int pred = -1;
   if (masked) {
@@ -206,9 +208,16 @@ __global__ __launch_bounds__(CM_THREADS) void unmask_commit(const Partial* __res
   const int nM = __popcll(mk);
   uint64_t sel = 0;
   if (nM > 0) {
-    sel = __ballot(masked && conf >= gamma);
-    const int left = num_steps - step;
-    const int k = (nM + left - 1) / left;  // completion floor
+    int k;
+    if (kind == TT_SAMPLER_PREDICT_NOISE) {
+      const int target = (S * (num_steps - 1 - step)) / num_steps;  // linear schedule
+      k = max(nM - target, 0);
+      sel = 0;
+    } else {
+      sel = __ballot(masked && conf >= gamma);
+      const int left = num_steps - step;
+      k = (nM + left - 1) / left;  // completion floor
+    }
     if (__popcll(sel) < k) {
       int rank = 0;  // place among the masked positions: higher conf first, then lower position
       for (int j = 0; j < S; ++j) {
@@ -230,28 +239,31 @@ __global__ __launch_bounds__(CM_THREADS) void unmask_commit(const Partial* __res
   }
 }
 
-// Host checks shared by the two unmask entry points.
+// Host checks shared by the unmask entry points.
 int unmask_check(const int32_t* tokens, const uint64_t* mask_bits, const int32_t* n_masked,
                  const size_t* workspace_bytes, int B, int S, int V, int step, int num_steps,
-                 float gamma, int mask_id) {
-  if (!tokens || !mask_bits || !n_masked || !workspace_bytes) return TT_ERR_ARG;
+                 int mask_id, const tt_sampler* sm) {
+  if (!tokens || !mask_bits || !n_masked || !workspace_bytes || !sm) return TT_ERR_ARG;
   if (B <= 0 || S <= 0 || V < 2) return TT_ERR_ARG;
   if (mask_id < 0 || mask_id >= V) return TT_ERR_ARG;
   if (num_steps <= 0 || step < 0 || step >= num_steps) return TT_ERR_ARG;
-  if (gamma != gamma) return TT_ERR_ARG;
+  if (sm->gamma != sm->gamma) return TT_ERR_ARG;
+  if (!(sm->temperature > 0.f) || !isfinite(sm->temperature)) return TT_ERR_ARG;
+  if (sm->kind != TT_SAMPLER_CONFIDENCE && sm->kind != TT_SAMPLER_PREDICT_NOISE) return TT_ERR_UNSUPPORTED;
   return TT_OK;
 }
 
+float sampler_scale(const tt_sampler* sm) { return TT_LOG2E / sm->temperature; }
+
 }  // namespace
 
-extern "C" int tt_confidence_unmask(const float* logits, int32_t* tokens, uint64_t* mask_bits,
-                                    int32_t* n_masked, float* conf_out, int32_t* pred_out, int B,
-                                    int S, int V, int step, int num_steps, float gamma,
-                                    int mask_id, void* workspace, size_t* workspace_bytes,
-                                    void* stream) {
+extern "C" int tt_unmask_sample(const float* logits, int32_t* tokens, uint64_t* mask_bits,
+                                int32_t* n_masked, float* conf_out, int32_t* pred_out, int B, int S,
+                                int V, int step, int num_steps, const tt_sampler* sampler, int mask_id,
+                                void* workspace, size_t* workspace_bytes, void* stream) {
   if (!logits) return TT_ERR_ARG;
-  int st = unmask_check(tokens, mask_bits, n_masked, workspace_bytes, B, S, V, step, num_steps, gamma,
-                        mask_id);
+  int st = unmask_check(tokens, mask_bits, n_masked, workspace_bytes, B, S, V, step, num_steps, mask_id,
+                        sampler);
   if (st != TT_OK) return st;
   if (S > 64) return TT_ERR_UNSUPPORTED;
   const size_t rows = (size_t)B * S;
@@ -263,29 +275,41 @@ extern "C" int tt_confidence_unmask(const float* logits, int32_t* tokens, uint64
   if ((uintptr_t)workspace % alignof(Partial)) return TT_ERR_ARG;
   hipStream_t s = (hipStream_t)stream;
   Partial* ws = (Partial*)workspace;
+  const float cs = sampler_scale(sampler);
   const bool vec4 = (V % 4 == 0) && ((uintptr_t)logits % 16 == 0);
   dim3 grid((unsigned)(rows * nchunk));
   if (vec4)
     hipLaunchKernelGGL(unmask_partial<true>, grid, dim3(UM_THREADS), 0, s, logits, mask_bits, ws,
-                       S, V, nchunk, mask_id);
+                       S, V, nchunk, mask_id, cs);
   else
     hipLaunchKernelGGL(unmask_partial<false>, grid, dim3(UM_THREADS), 0, s, logits, mask_bits, ws,
-                       S, V, nchunk, mask_id);
+                       S, V, nchunk, mask_id, cs);
   if (tt_launch_status() != TT_OK) return TT_ERR_HIP;
   hipLaunchKernelGGL(unmask_commit, dim3(B), dim3(CM_THREADS), 0, s, ws, tokens, mask_bits, n_masked,
-                     conf_out, pred_out, S, nchunk, step, num_steps, gamma);
+                     conf_out, pred_out, S, nchunk, step, num_steps, sampler->kind, sampler->gamma, cs);
   return tt_launch_status();
+}
+
+extern "C" int tt_confidence_unmask(const float* logits, int32_t* tokens, uint64_t* mask_bits,
+                                    int32_t* n_masked, float* conf_out, int32_t* pred_out, int B,
+                                    int S, int V, int step, int num_steps, float gamma,
+                                    int mask_id, void* workspace, size_t* workspace_bytes,
+                                    void* stream) {
+  const tt_sampler sm{TT_SAMPLER_CONFIDENCE, gamma, 1.f};
+  return tt_unmask_sample(logits, tokens, mask_bits, n_masked, conf_out, pred_out, B, S, V, step, num_steps,
+                          &sm, mask_id, workspace, workspace_bytes, stream);
 }
 
 extern "C" int tt_lmhead_unmask(const void* hidden, const void* w, const int32_t* bias_tok,
                                 const float* bias_val, int32_t* tokens, uint64_t* mask_bits,
                                 int32_t* n_masked, float* conf_out, int32_t* pred_out, int B, int S,
-                                int H, int V, int step, int num_steps, float gamma, int mask_id,
-                                int dtype, void* workspace, size_t* workspace_bytes, void* stream) {
+                                int H, int V, int step, int num_steps, const tt_sampler* sampler,
+                                int mask_id, int dtype, void* workspace, size_t* workspace_bytes,
+                                void* stream) {
   if (!hidden || !w) return TT_ERR_ARG;
   if ((bias_tok == nullptr) != (bias_val == nullptr)) return TT_ERR_ARG;
-  int st = unmask_check(tokens, mask_bits, n_masked, workspace_bytes, B, S, V, step, num_steps, gamma,
-                        mask_id);
+  int st = unmask_check(tokens, mask_bits, n_masked, workspace_bytes, B, S, V, step, num_steps, mask_id,
+                        sampler);
   if (st != TT_OK) return st;
   if (H <= 0) return TT_ERR_ARG;
   if (dtype != TT_F32 && dtype != TT_BF16) return TT_ERR_UNSUPPORTED;
@@ -303,12 +327,13 @@ extern "C" int tt_lmhead_unmask(const void* hidden, const void* w, const int32_t
   hipStream_t s = (hipStream_t)stream;
   Partial* parts = (Partial*)workspace;
   Partial* rowres = (Partial*)((char*)workspace + parts_bytes);
-  const TtRedArgs red{bias_tok, bias_val, mask_id, parts, nparts, mask_bits, S, B};
+  const float cs = sampler_scale(sampler);
+  const TtRedArgs red{bias_tok, bias_val, mask_id, parts, nparts, mask_bits, S, B, cs};
   if (tt_lm_reduce_launch(hidden, w, M, H, V, red, s) != TT_OK) return TT_ERR_HIP;
   hipLaunchKernelGGL(unmask_rowmerge, dim3((unsigned)M), dim3(UM_THREADS), 0, s, parts, mask_bits, rowres,
-                     S, nparts);
+                     S, nparts, cs);
   if (tt_launch_status() != TT_OK) return TT_ERR_HIP;
   hipLaunchKernelGGL(unmask_commit, dim3(B), dim3(CM_THREADS), 0, s, rowres, tokens, mask_bits, n_masked,
-                     conf_out, pred_out, S, 1, step, num_steps, gamma);
+                     conf_out, pred_out, S, 1, step, num_steps, sampler->kind, sampler->gamma, cs);
   return tt_launch_status();
 }

@@ -36,6 +36,15 @@ extern "C" {
 
 enum tt_dtype { TT_F32 = 0, TT_BF16 = 1 };
 
+/* Commit rules of an unmasking step (see tt_unmask_sample). */
+enum tt_sampler_kind { TT_SAMPLER_CONFIDENCE = 0, TT_SAMPLER_PREDICT_NOISE = 1 };
+
+typedef struct tt_sampler {
+  int kind;            /* enum tt_sampler_kind */
+  float gamma;         /* TT_SAMPLER_CONFIDENCE: commit threshold on the confidence */
+  float temperature;   /* > 0: confidences are max softmax(logits / temperature); 1 = plain */
+} tt_sampler;
+
 enum tt_status {
   TT_OK = 0,
   TT_ERR_ARG = -1,          /* invalid argument (null pointer, bad size, NaN parameter, ...) */
@@ -155,7 +164,7 @@ int tt_confidence_unmask(const float* logits, int32_t* tokens, uint64_t* mask_bi
  * stored ("Nemotron-Labs-TwoTower" wiki page, section "Block-wise generation": the step needs,
  * per masked position, only the top probability and its token).
  *
- * Computes what tt_confidence_unmask computes on the logits
+ * Computes what tt_unmask_sample (with the given host `sampler`) computes on the logits
  *   l[m][v] = sum_k hidden[m][k] * w[v][k]  (+ bias_val[m] when v == bias_tok[m])
  * for m = b*S + i. The optional bias adds one value to one vocabulary entry per row (a logit bias
  * such as a forced or banned token); bias_tok[m] outside [0, V) adds nothing. Both bias
@@ -165,7 +174,7 @@ int tt_confidence_unmask(const float* logits, int32_t* tokens, uint64_t* mask_bi
  * Results: equal to the two-call path up to fp32 rounding order of the softmax sum (the logits
  *   themselves are the same fp32 accumulators); deterministic run to run.
  * Supported: dtype TT_BF16, H % 64 == 0, 1 <= S <= 64.
- * Errors: those of tt_confidence_unmask; TT_ERR_ARG also for null hidden / w, H <= 0, exactly one
+ * Errors: those of tt_unmask_sample; TT_ERR_ARG also for null hidden / w, H <= 0, exactly one
  *   bias pointer NULL, hidden or w not 16-byte aligned; TT_ERR_UNSUPPORTED for dtype TT_F32,
  *   H % 64 != 0 or S > 64.
  * Workspace: one 16-byte record per (row, block of 32 to 128 vocabulary columns, by B*S) plus one
@@ -174,9 +183,34 @@ int tt_confidence_unmask(const float* logits, int32_t* tokens, uint64_t* mask_bi
 int tt_lmhead_unmask(const void* hidden, const void* w, const int32_t* bias_tok,
                      const float* bias_val, int32_t* tokens, uint64_t* mask_bits,
                      int32_t* n_masked, float* conf_out, int32_t* pred_out,
-                     int B, int S, int H, int V, int step, int num_steps, float gamma,
-                     int mask_id, int dtype, void* workspace, size_t* workspace_bytes,
-                     void* stream);
+                     int B, int S, int H, int V, int step, int num_steps,
+                     const tt_sampler* sampler, int mask_id, int dtype, void* workspace,
+                     size_t* workspace_bytes, void* stream);
+
+/*
+ * tt_unmask_sample — tt_confidence_unmask with a choice of sampler (the sampler variants of
+ * "Nemotron-Labs-TwoTower" wiki page, section "Block-wise generation", and its model-card
+ * example's temperature 0.1).
+ *
+ *   conf_i = max softmax(logits row / temperature) (mask id excluded), pred_i = its lowest
+ *            argmax (temperature never changes pred_i);
+ *   TT_SAMPLER_CONFIDENCE:    commit exactly as tt_confidence_unmask with this gamma (and
+ *                             tt_confidence_unmask is this call with temperature 1);
+ *   TT_SAMPLER_PREDICT_NOISE: the block-diffusion predict-and-noise sampler: with a linear noise
+ *                             schedule, target = floor(S (num_steps - 1 - step) / num_steps)
+ *                             positions stay masked after the step, so the
+ *                             max(|Mk| - target, 0) most confident masked positions commit (ties:
+ *                             lower position first); gamma is not used.
+ * The schedule over S (not over the masked count) and its linearity are this library's reading:
+ * the page names the sampler, not its schedule.
+ * Arguments, layouts, workspace and errors as tt_confidence_unmask, plus: `sampler` is a HOST
+ * pointer, read before the call returns; TT_ERR_ARG for a null sampler, a temperature that is
+ * not finite and positive, or a NaN gamma; TT_ERR_UNSUPPORTED for an unknown kind.
+ */
+int tt_unmask_sample(const float* logits, int32_t* tokens, uint64_t* mask_bits,
+                     int32_t* n_masked, float* conf_out, int32_t* pred_out,
+                     int B, int S, int V, int step, int num_steps, const tt_sampler* sampler,
+                     int mask_id, void* workspace, size_t* workspace_bytes, void* stream);
 
 /* Human-readable name of a status code (static string). */
 const char* tt_status_string(int status);

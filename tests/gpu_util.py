@@ -49,7 +49,15 @@ def committed(before: int, after: int, S: int):
     return [i for i in range(S) if (before >> i) & 1 and not (after >> i) & 1]
 
 
-def check_commit_step(S, gamma, step, T, bits_before, tokens_before, gpu, ref):
+def floor_k(kind, n, S, step, T):
+    """Number of positions the step must commit at least: the completion floor (confidence
+    sampler) or the noise schedule's count (predict-and-noise)."""
+    if kind == "predict_noise":
+        return max(n - (S * (T - 1 - step)) // T, 0)
+    return -(-n // (T - step))
+
+
+def check_commit_step(S, gamma, step, T, bits_before, tokens_before, gpu, ref, kind="confidence"):
     """Compare one unmask step. gpu/ref: dicts with tokens [B][S], mask_bits [B] (uint64),
     n_masked [B], conf [B][S], pred [B][S]. Returns the number of blocks with an exempt
     divergence (0 when bit-exact). Raises AssertionError on a non-exempt difference."""
@@ -70,11 +78,11 @@ def check_commit_step(S, gamma, step, T, bits_before, tokens_before, gpu, ref):
             diff = set(cg) ^ set(cr)
             masked = [i for i in range(S) if (before >> i) & 1]
             confs = sorted((float(ref["conf"][b][i]) for i in masked), reverse=True)
-            k = -(-len(masked) // (T - step))
-            kth = confs[min(k, len(confs)) - 1]
+            k = floor_k(kind, len(masked), S, step, T)
+            kth = confs[min(max(k, 1), len(confs)) - 1]
             for i in diff:
                 c = float(ref["conf"][b][i])
-                near_gamma = abs(c - gamma) <= GAMMA_BAND
+                near_gamma = kind == "confidence" and abs(c - gamma) <= GAMMA_BAND
                 near_tie = abs(c - kth) <= TIE_REL * max(abs(kth), 1e-30)
                 assert near_gamma or near_tie, (b, i, c, gamma, cg, cr)
             exempt_blocks += 1
@@ -85,7 +93,7 @@ def check_commit_step(S, gamma, step, T, bits_before, tokens_before, gpu, ref):
     return exempt_blocks
 
 
-def check_fused_step(S, gamma, step, T, bits_before, gpu, ref, logits_of, mask_id, blocks):
+def check_fused_step(S, gamma, step, T, bits_before, gpu, ref, logits_of, mask_id, blocks, kind="confidence"):
     """Compare one fused LM-head + unmask step on the given blocks. logits_of(row) returns the
     oracle's fp64 logits row (bias included). Returns (number of blocks with an exempt commit
     divergence, relative confidence errors of all masked positions checked)."""
@@ -112,11 +120,12 @@ def check_fused_step(S, gamma, step, T, bits_before, gpu, ref, logits_of, mask_i
         if cg != cr:
             masked = [i for i in range(S) if (before >> i) & 1]
             confs = sorted((float(ref["conf"][b][i]) for i in masked), reverse=True)
-            k = -(-len(masked) // (T - step))
-            kth = confs[min(k, len(confs)) - 1]
+            k = floor_k(kind, len(masked), S, step, T)
+            kth = confs[min(max(k, 1), len(confs)) - 1]
             for i in set(cg) ^ set(cr):
                 c = float(ref["conf"][b][i])
-                assert abs(c - gamma) <= GAMMA_BAND or abs(c - kth) <= CONF_TIE_FUSED, (b, i, c, gamma, cg, cr)
+                near_gamma = kind == "confidence" and abs(c - gamma) <= GAMMA_BAND
+                assert near_gamma or abs(c - kth) <= CONF_TIE_FUSED, (b, i, c, gamma, cg, cr)
             exempt_blocks += 1
             continue
         assert int(gpu["mask_bits"][b]) == int(ref["mask_bits"][b])

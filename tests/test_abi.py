@@ -133,8 +133,9 @@ def _fu(ws=None, nbytes=0, **kw):
              gamma=0.8, mask_id=3, dtype=_lib.TT_BF16)
     a.update(kw)
     n = ctypes.c_size_t(nbytes)
+    sm = _lib.Sampler(a.get("kind", 0), a["gamma"], a.get("temp", 1.0))
     st = _lib.load().tt_lmhead_unmask(a["h"], a["w"], a["bt"], a["bv"], a["tok"], a["bits"], a["nm"], None, None,
-                                      a["B"], a["S"], a["H"], a["V"], a["step"], a["T"], a["gamma"],
+                                      a["B"], a["S"], a["H"], a["V"], a["step"], a["T"], ctypes.byref(sm),
                                       a["mask_id"], a["dtype"], ws, ctypes.byref(n), None)
     return st, n.value
 
@@ -155,6 +156,7 @@ def test_fused_workspace_query():
     (dict(bt=P), -1), (dict(bv=P), -1), (dict(B=0), -1), (dict(S=0), -1), (dict(H=0), -1), (dict(V=1), -1),
     (dict(mask_id=131072), -1), (dict(step=16), -1), (dict(gamma=float("nan")), -1),
     (dict(dtype=_lib.TT_F32), -2), (dict(dtype=7), -2), (dict(H=2656), -2), (dict(S=65), -2),
+    (dict(temp=0.0), -1), (dict(temp=-1.0), -1), (dict(temp=float("inf")), -1), (dict(kind=2), -2),
 ])
 def test_fused_argument_errors(kw, code):
     assert _fu(**kw)[0] == code
@@ -189,3 +191,28 @@ def test_context_extend_workspace_matches_block_attention():
 ])
 def test_context_extend_argument_errors(kw, code):
     assert _ce(**kw)[0] == code
+
+
+def _us(ws=None, nbytes=0, sampler=True, **kw):
+    a = dict(lg=P, tok=P, bits=P, nm=P, B=1, S=16, V=131072, step=0, T=16, mask_id=3, kind=0, gamma=0.8, temp=1.0)
+    a.update(kw)
+    n = ctypes.c_size_t(nbytes)
+    sm = _lib.Sampler(a["kind"], a["gamma"], a["temp"])
+    st = _lib.load().tt_unmask_sample(a["lg"], a["tok"], a["bits"], a["nm"], None, None, a["B"], a["S"], a["V"],
+                                      a["step"], a["T"], ctypes.byref(sm) if sampler else None, a["mask_id"], ws,
+                                      ctypes.byref(n), None)
+    return st, n.value
+
+
+def test_unmask_sample_workspace_equals_confidence_unmask():
+    for kind, temp in ((0, 1.0), (1, 0.1), (0, 2.5)):
+        st, n = _us(kind=kind, temp=temp)
+        assert st == 0 and n == _um()[1]
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(sampler=False), -1), (dict(temp=0.0), -1), (dict(temp=float("nan")), -1), (dict(gamma=float("nan")), -1),
+    (dict(kind=-1), -2), (dict(kind=7), -2), (dict(lg=None), -1), (dict(S=65), -2), (dict(step=16), -1),
+])
+def test_unmask_sample_argument_errors(kw, code):
+    assert _us(**kw)[0] == code
