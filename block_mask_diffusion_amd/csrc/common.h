@@ -131,18 +131,32 @@ __device__ __forceinline__ void tt_dma16_nt(const void* gptr, uint32_t lds_base)
 }
 
 // The same with the LDS address given as a base plus a constant byte offset, added into M0 inside
-// the asm: a loop that fills many slots from one base keeps a single scalar register live.
-template <int OFF>
+// the asm: a loop that fills many slots from one base keeps a single scalar register live. NT
+// selects the non-temporal policy.
+template <int OFF, bool NT = false>
 __device__ __forceinline__ void tt_dma16_at(const void* gptr, uint32_t lds_base) {
   uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_add_u32 m0, %2, %3\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
-      "s_nop 0\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(gptr), "s"(lds_base), "i"(OFF)
-      : "memory", "scc");
+  if constexpr (NT) {
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_add_u32 m0, %2, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off nt\n\t"
+        "s_nop 0\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(gptr), "s"(lds_base), "i"(OFF)
+        : "memory", "scc");
+  } else {
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_add_u32 m0, %2, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_nop 0\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(gptr), "s"(lds_base), "i"(OFF)
+        : "memory", "scc");
+  }
 }
