@@ -1,7 +1,7 @@
-// LM-head product for many hidden rows (M > 64) ("Nemotron-Labs-TwoTower" wiki page, section
+// LM-head product for more than 16 hidden rows ("Nemotron-Labs-TwoTower" wiki page, section
 // "Block-wise generation": every denoising step predicts all masked positions of every block in
-// parallel). At these sizes re-reading the hidden rows from L2 and the matrix cores, rather than
-// streaming W, set the pace.
+// parallel). Up to a hundred-odd rows the W stream from HBM sets the pace; from a few hundred
+// rows on, the matrix cores and the re-reads of the hidden rows from L2 do.
 //
 // Built with the iterative ILP machine scheduler (see build.py): with one wave per SIMD the
 // kernel relies on the next k-step's LDS reads being in flight while the current MFMAs run,

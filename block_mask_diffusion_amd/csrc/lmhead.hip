@@ -466,18 +466,13 @@ int lm_lds_launch(const void* hidden, const void* w, float* logits, int M, int H
 template <int MT, int BMT, int VT, int KW, bool NT, int NSET>
 constexpr int lds_cols_per_part() { return VT * Shape<bf16, MT>::NV; }
 
-// Kernel choice (measured on MI355X at H = 2688, V = 131072): M <= 64 the LDS-staged kernel
-// <MT, BMT, VT, KW, NT, NSET> per hidden-row bucket; M > 64 the MFMA GEMM kernel (gemm.hip);
-// the direct kernel <MT, BMT, VT, STEP, RING, KCH> for fp32 and for H not a multiple of the
-// stage width.
+// Kernel choice (measured on MI355X at H = 2688, V = 131072): M <= 16 the LDS-staged kernel
+// <MT, BMT, VT, KW, NT, NSET>; larger M the MFMA GEMM kernel (gemm.hip), which with its
+// non-temporal W stream beats the LDS-staged kernel from 17 rows on (123 against 137 us at 64
+// rows); the direct kernel <MT, BMT, VT, STEP, RING, KCH> for fp32 and for H not a multiple of
+// the stage width.
 #ifndef TT_LM_LDS16
 #define TT_LM_LDS16 16, 1, 4, 64, true, 4
-#endif
-#ifndef TT_LM_LDS64
-#define TT_LM_LDS64 16, 4, 2, 64, true, 4
-#endif
-#ifndef TT_LM_LDS128
-#define TT_LM_LDS128 32, 4, 1, 64, true, 4
 #endif
 #ifndef TT_LM_CFG32
 #define TT_LM_CFG32 32, 1, 2, 32, 8, 256
@@ -502,16 +497,10 @@ int lm_direct(const void* h, const void* w, float* o, int M, int H, int V, hipSt
   return lm_launch<bf16, MT, BMT, VT, STEP, RING, KCH>(h, w, o, M, H, V, s);
 }
 
-#ifndef TT_GEMM_MIN_M
-#define TT_GEMM_MIN_M 65
-#endif
-
 int lm_bf16(const void* h, const void* w, float* o, int M, int H, int V, hipStream_t s) {
-  if (M >= TT_GEMM_MIN_M && H % TT_GEMM_KB == 0) return tt_lm_gemm_launch(h, w, o, M, H, V, s);
+  if (M > 16 && H % TT_GEMM_KB == 0) return tt_lm_gemm_launch(h, w, o, M, H, V, s);
   int st = 1;
   if (M <= 16) st = lm_try_lds<TT_LM_LDS16>(h, w, o, M, H, V, s);
-  else if (M <= 64) st = lm_try_lds<TT_LM_LDS64>(h, w, o, M, H, V, s);
-  else if (M <= 128) st = lm_try_lds<TT_LM_LDS128>(h, w, o, M, H, V, s);
   if (st != 1) return st;
   if (M <= 32) return lm_direct<TT_LM_CFG32>(h, w, o, M, H, V, s);
   if (M <= 64) return lm_direct<TT_LM_CFG64>(h, w, o, M, H, V, s);
@@ -521,19 +510,15 @@ int lm_bf16(const void* h, const void* w, float* o, int M, int H, int V, hipStre
 }  // namespace
 
 // Fused LM head + vocabulary reduction (bf16, H % 64 == 0): which kernel, and how many records per
-// row it writes. M <= 16 and M <= 64 use the LDS-staged kernel of the same bucket as the logits
-// path, larger M the GEMM kernel (128 columns per record).
+// row it writes. The same kernel and tile as the logits path for each M (so the accumulators are
+// the same): M <= 16 the LDS-staged kernel, larger M the GEMM kernel (128 columns per record).
 int tt_lm_reduce_nparts(int M, int V) {
-  int cols;
-  if (M <= 16) cols = lds_cols_per_part<TT_LM_LDS16>();
-  else if (M <= 64) cols = lds_cols_per_part<TT_LM_LDS64>();
-  else cols = 128;
+  const int cols = M <= 16 ? lds_cols_per_part<TT_LM_LDS16>() : 128;
   return (V + cols - 1) / cols;
 }
 
 int tt_lm_reduce_launch(const void* hidden, const void* w, int M, int H, int V, TtRedArgs red, hipStream_t s) {
   if (M <= 16) return lm_lds_launch<TT_LM_LDS16, true>(hidden, w, nullptr, M, H, V, s, red);
-  if (M <= 64) return lm_lds_launch<TT_LM_LDS64, true>(hidden, w, nullptr, M, H, V, s, red);
   return tt_lm_gemm_reduce_launch(hidden, w, M, H, V, red, s);
 }
 

@@ -8,7 +8,7 @@
 #define TT_GEMM_KB 64
 #endif
 
-// Launches the MFMA GEMM LM-head kernel (bf16, H % TT_GEMM_KB == 0; used for M > 64) on stream s.
+// Launches the MFMA GEMM LM-head kernel (bf16, H % TT_GEMM_KB == 0; used for M > 16) on stream s.
 __attribute__((visibility("hidden"))) int tt_lm_gemm_launch(const void* hidden, const void* w,
                                                             float* logits, int M, int H, int V,
                                                             hipStream_t s);

@@ -141,8 +141,8 @@ def _fu(ws=None, nbytes=0, **kw):
 
 
 def test_fused_workspace_query():
-    # records per row: 64 columns each for up to 16 rows, 32 for up to 64, 128 beyond; plus one per row
-    for B, cols in ((1, 64), (4, 32), (5, 128), (32, 128)):
+    # records per row: 64 columns each for up to 16 rows, 128 beyond; plus one per row
+    for B, cols in ((1, 64), (4, 128), (5, 128), (32, 128)):
         M = 16 * B
         st, n = _fu(B=B)
         assert st == 0 and n == M * (131072 // cols) * 16 + M * 16, (B, n)
