@@ -148,11 +148,15 @@ struct Scan {
   int tmp[NT];
 };
 
-// Exclusive prefix sums of N_b = ctx_len[b] + S into sc.pb[0..B] (B <= AT_MAX_B), NT threads.
+// Exclusive prefix sums of N_b = ctx_len[b] + S into sc.pb[0..B] (B <= AT_MAX_B), NT threads:
+// thread t sums its PER consecutive lengths, a shuffle scan runs inside each wave, and the wave
+// totals are added through LDS (two barriers).
 template <int NT>
 __device__ void scan_lengths(Scan<NT>& sc, const int32_t* __restrict__ ctx_len, int B, int S) {
   const int t = threadIdx.x;
   constexpr int PER = AT_MAX_B / NT;
+  constexpr int NW = NT / TT_WAVE;
+  static_assert(NW <= TT_WAVE, "wave totals fit one wave");
   int v[PER];
   int loc = 0;
 #pragma unroll
@@ -161,15 +165,18 @@ __device__ void scan_lengths(Scan<NT>& sc, const int32_t* __restrict__ ctx_len, 
     v[k] = (b < B) ? ctx_len[b] + S : 0;
     loc += v[k];
   }
-  sc.tmp[t] = loc;
-  __syncthreads();
-  for (int off = 1; off < NT; off <<= 1) {  // Hillis-Steele inclusive scan
-    int x = (t >= off) ? sc.tmp[t - off] : 0;
-    __syncthreads();
-    sc.tmp[t] += x;
-    __syncthreads();
+  const int lane = t & (TT_WAVE - 1), wv = t / TT_WAVE;
+  int inc = loc;  // inclusive scan of loc inside the wave
+#pragma unroll
+  for (int off = 1; off < TT_WAVE; off <<= 1) {
+    const int x = __shfl_up(inc, off, TT_WAVE);
+    if (lane >= off) inc += x;
   }
-  int run = sc.tmp[t] - loc;
+  if (lane == TT_WAVE - 1) sc.tmp[wv] = inc;
+  __syncthreads();
+  int before = 0;  // totals of the waves before this one
+  for (int k = 0; k < wv; ++k) before += sc.tmp[k];
+  int run = before + inc - loc;
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
     sc.pb[t * PER + k] = run;
