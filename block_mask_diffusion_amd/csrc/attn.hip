@@ -31,20 +31,13 @@
 
 namespace {
 
-#ifndef TT_AT_TPW
-#define TT_AT_TPW 1
-#endif
-#ifndef TT_AT_PRIO
-#define TT_AT_PRIO 1
-#endif
-constexpr int TPW = TT_AT_TPW;  // query tiles per wave (each K/V fragment read feeds TPW MFMAs)
-constexpr int AT_THREADS = 512 / TPW;
+constexpr int AT_THREADS = 512;
 constexpr int AT_WAVES = AT_THREADS / TT_WAVE;
-constexpr int QT = 32;          // query rows per MFMA tile
+constexpr int QT = 32;          // query rows per MFMA tile, one tile per wave
 constexpr int MAX_ROWS = 256;   // S*G limit: 8 tiles
 constexpr int AT_MAX_B = 1024;  // sequences handled by the in-workgroup prefix scan
 constexpr float LOG2E = 1.4426950408889634f;
-static_assert(MAX_ROWS == QT * TPW * AT_WAVES, "8 query tiles per workgroup");
+static_assert(MAX_ROWS == QT * AT_WAVES, "8 query tiles per workgroup");
 constexpr float RESCALE_LOG2 = 8.f;  // lazy-rescale threshold (log2 units)
 // K/V stage loads: every key row is read exactly once, so they stream with the non-temporal
 // policy
@@ -63,28 +56,9 @@ struct Mf<bf16> {
   __device__ static __forceinline__ f32x16 mma(frag a, frag b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
-  // P^T operand of MFMA u: score registers 8u..8u+7, rounded to bf16. Register j of lane half h
-  // holds key 8(j/4) + 4h + j%4 of the sub-tile, i.e. keys 16u + 4h + {0..3} and 16u + 8 + 4h +
-  // {0..3}; the V^T operand is read in the same key order.
-  __device__ static __forceinline__ frag pfrag(const f32x16& p, int u) {
-    frag f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) f[i] = (bf16)p[8 * u + i];
-    return f;
-  }
-  // acc + sum of the 16 bf16 probabilities of this lane, by pairs (v_dot2 with (1, 1))
-  __device__ static __forceinline__ float psum(const frag (&pf)[2], const f32x16&, float acc) {
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    const bf16x2 one = {(bf16)1.f, (bf16)1.f};
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[u], pf[u], 0, 1), one, acc, false);
-      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[u], pf[u], 2, 3), one, acc, false);
-      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[u], pf[u], 4, 5), one, acc, false);
-      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[u], pf[u], 6, 7), one, acc, false);
-    }
-    return acc;
-  }
+  // The P^T operand of MFMA u holds score registers 8u..8u+7, rounded to bf16. Register j of
+  // lane half h holds key 8(j/4) + 4h + j%4 of the sub-tile, i.e. keys 16u + 4h + {0..3} and
+  // 16u + 8 + 4h + {0..3}; the V^T operand is read in the same key order.
 };
 
 template <>
@@ -95,15 +69,8 @@ struct Mf<float> {
   __device__ static __forceinline__ f32x16 mma(frag a, frag b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
   }
-  // register u of lane half h holds key 8(u/4) + 4h + u%4 and feeds reduction slot 2u + h
-  __device__ static __forceinline__ frag pfrag(const f32x16& p, int u) { return p[u]; }
-  template <int N>
-  __device__ static __forceinline__ float psum(const frag (&)[N], const f32x16& p, float acc) {
-    float s = 0.f;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) s += p[j];
-    return acc + s;
-  }
+  // The P^T operand of MFMA u is score register u: key 8(u/4) + 4h + u%4 for lane half h,
+  // reduction slot 2u + h.
 };
 
 // Stage geometry: KC keys per stage (64 for bf16, 32 for fp32), K and V stored row-major in an
@@ -111,7 +78,8 @@ struct Mf<float> {
 template <typename T>
 constexpr int kc_of() { return sizeof(T) == 2 ? 64 : 32; }
 constexpr int NBUF = 4;
-constexpr int PD = NBUF - 1;  // stages whose loads run ahead
+constexpr int PD = 2;  // stages whose loads run ahead (two more are in use: K is read one
+                       // sub-tile ahead of V)
 
 template <typename T, int D>
 struct Geo {
@@ -228,6 +196,13 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_partial(Args<T, D> A) {
   constexpr int KS = MF::KS, EPL = MF::EPL, KC = GE::KC, RB = GE::RB, GPR = GE::GPR;
   constexpr int SPS = KC / 32;                  // 32-key sub-tiles per stage
   constexpr int CPW = GE::NCH / AT_WAVES;       // K (and V) chunks per wave per stage
+  constexpr int NQK = D / KS;                   // MFMAs of one sub-tile's scores
+  constexpr int NDT = D / 32;                   // 32-wide d tiles of the output
+  constexpr int NUU = 32 / KS;                  // MFMAs per d tile of one sub-tile's PV product
+  constexpr int NPV = NDT * NUU;
+  // bf16: software-pipelined sub-tile loop. fp32 (32 registers of operands per MFMA tile more)
+  // runs the sub-tiles one after the other, which keeps it within the register file.
+  constexpr bool PIPE = EPL == 8;
 
   __shared__ Ring<T, D> ring;
   __shared__ Scan<AT_THREADS> sc;
@@ -241,7 +216,7 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_partial(Args<T, D> A) {
   const int G = A.Hq / A.Hkv;
   const int R = A.S * G;
   const int U = A.B * A.Hkv;
-  const bool active = wave * TPW * QT < R;  // this wave owns query rows [32*TPW*wave, +32*TPW)
+  const bool active = wave * QT < R;  // this wave owns query rows [32 wave, 32 wave + 32)
 
   scan_lengths<AT_THREADS>(sc, A.ctx_len, A.B, A.S);
   const int64_t Ttot = (int64_t)A.Hkv * sc.pb[A.B];
@@ -261,6 +236,37 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_partial(Args<T, D> A) {
   }
   int u = b * A.Hkv + (int)((lo - (int64_t)A.Hkv * sc.pb[b]) / (sc.pb[b + 1] - sc.pb[b]));
 
+  // Per-lane byte offsets that are the same for every piece, stage and sub-tile (bf16 path): the
+  // K and V^T fragment reads inside a stage slot (the slot and the sub-tile add constants, since
+  // the swizzles repeat every 16 rows and sub-tiles are 32 rows apart), and the stage loads'
+  // sources relative to the stage's first key row.
+  static_assert(!PIPE || (32 % (GE::RPW * (GE::GMASK + 1)) == 0), "K swizzle repeats within 32 rows");
+  typedef __attribute__((address_space(3))) const unsigned char* lds_cptr;
+  lds_cptr koff[NQK], voff[NDT];
+  uint32_t dkoff[CPW], dvoff[CPW];
+  uint32_t lds_k0 = 0;  // LDS address of this wave's first load chunk in stage slot 0 (K)
+  if constexpr (PIPE) {
+    const unsigned char* rk = &ring.k[0][0];
+    const unsigned char* rv = &ring.v[0][0];
+#pragma unroll
+    for (int ks = 0; ks < NQK; ++ks)
+      koff[ks] = TT_LDS_PTR(const unsigned char, rk + l32 * RB + 16 * ((2 * ks + hh2) ^ GE::fk(l32)));
+    const int G4 = lane >> 4, jj = lane & 15;
+    const int r0 = 4 * (G4 >> 1) + (jj >> 2);  // + 32 kt + 16 uu + 8 rd: same V swizzle
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const int d = dt * 32 + 16 * (G4 & 1) + 4 * (jj & 3);
+      voff[dt] = TT_LDS_PTR(const unsigned char, rv + r0 * RB + 16 * ((d >> 3) ^ GE::fv(r0)) + 2 * (d & 7));
+    }
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      const int r = (wave * CPW + c) * GE::RPC + lane / GPR, slot = lane % GPR;
+      dkoff[c] = r * RB + 16 * (slot ^ GE::fk(r));
+      dvoff[c] = r * RB + 16 * (slot ^ GE::fv(r));
+    }
+    lds_k0 = tt_lds_addr(&ring.k[0][wave * CPW * 1024]);
+  }
+
   for (; u < U; ++u) {
     const int bb = u / A.Hkv, g = u - bb * A.Hkv;
     const int N = sc.pb[bb + 1] - sc.pb[bb];
@@ -276,37 +282,35 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_partial(Args<T, D> A) {
     const T* kblk = A.kb + ((size_t)bb * A.S * A.Hkv + g) * D;
     const T* vblk = A.vb + ((size_t)bb * A.S * A.Hkv + g) * D;
 
-    // ---- query fragments (B operand of S^T = K Q^T): lane holds row `row`
-    frag qf[TPW][D / KS];
-#pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-      const int row = (wave * TPW + t) * QT + l32;
-      const bool ok = active && row < R;
-      const int s = ok ? row / G : 0, hq = ok ? g * G + row % G : 0;
+    // ---- query fragments (B operand of S^T = K Q^T): lane holds query row `row` of the unit
+    const int row = wave * QT + l32;
+    const bool row_ok = active && row < R;
+    frag qf[NQK];
+    {
+      const int s = row_ok ? row / G : 0, hq = row_ok ? g * G + row % G : 0;
       const T* qp = A.q + (((size_t)bb * A.S + s) * A.Hq + hq) * D;
 #pragma unroll
-      for (int ks = 0; ks < D / KS; ++ks) {
-        if (ok) {
-          if constexpr (EPL == 8) qf[t][ks] = *reinterpret_cast<const frag*>(qp + KS * ks + EPL * hh2);
-          else qf[t][ks] = qp[KS * ks + hh2];
+      for (int ks = 0; ks < NQK; ++ks) {
+        if (row_ok) {
+          if constexpr (EPL == 8) qf[ks] = *reinterpret_cast<const frag*>(qp + KS * ks + EPL * hh2);
+          else qf[ks] = qp[KS * ks + hh2];
         } else {
-          if constexpr (EPL == 8) { for (int i = 0; i < 8; ++i) qf[t][ks][i] = (bf16)0.f; }
-          else qf[t][ks] = 0.f;
+          if constexpr (EPL == 8) { for (int i = 0; i < 8; ++i) qf[ks][i] = (bf16)0.f; }
+          else qf[ks] = 0.f;
         }
       }
+      // Wait for the query loads here, on every path, with a wait the compiler sees: otherwise
+      // its wait-count pass may place a full vmcnt(0) wait inside the sub-tile loop (it does not
+      // see the stage loads, which are inline asm), and that would drain the stage prefetch.
+      __builtin_amdgcn_s_waitcnt(TT_WAIT_VMCNT0);
     }
 
-    f32x16 o[TPW][D / 32];
-    float mrun[TPW], lrun[TPW];
+    f32x16 o[NDT];
+    float mrun = -INFINITY, lrun = 0.f;
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-      mrun[t] = -INFINITY;
-      lrun[t] = 0.f;
+    for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) o[t][dt][j] = 0.f;
-    }
+      for (int j = 0; j < 16; ++j) o[dt][j] = 0.f;
 
     // ---- stage loads: global -> LDS directly
     const int nkeys = ke - ka;
@@ -361,12 +365,13 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_partial(Args<T, D> A) {
       tt_lds_barrier();
     };
 
-    auto kread = [&](const unsigned char* kb_, int kt, frag (&kf)[D / KS]) {
+    // K fragments (A operand of S^T = K Q^T) of sub-tile kt of a stage: lane holds key 32kt + l32
+    auto kread = [&](const unsigned char* kb_, int kt, frag (&kf)[NQK]) {
       const int r = kt * 32 + l32;
       const unsigned char* rp = kb_ + r * RB;
       const int f = GE::fk(r);
 #pragma unroll
-      for (int ks = 0; ks < D / KS; ++ks) {
+      for (int ks = 0; ks < NQK; ++ks) {
         if constexpr (EPL == 8) {
           kf[ks] = *reinterpret_cast<const frag*>(rp + 16 * ((2 * ks + hh2) ^ f));
         } else {
@@ -374,20 +379,6 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_partial(Args<T, D> A) {
           kf[ks] = *reinterpret_cast<const float*>(rp + 16 * ((d >> 2) ^ f) + 4 * (d & 3));
         }
       }
-    };
-    auto qk = [&](const frag (&kf)[D / KS], f32x16 (&acc)[TPW]) {
-#pragma unroll
-      for (int t = 0; t < TPW; ++t)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) acc[t][j] = 0.f;
-      if (TT_AT_PRIO) __builtin_amdgcn_s_setprio(2);  // MFMA phase: let this wave issue first
-      // one accumulation chain per tile: back-to-back MFMAs into the same accumulator need no
-      // extra wait states, and a second chain would cost 16 adds to merge
-#pragma unroll
-      for (int ks = 0; ks < D / KS; ++ks)
-#pragma unroll
-        for (int t = 0; t < TPW; ++t) acc[t] = MF::mma(kf[ks], qf[t][ks], acc[t]);
-      if (TT_AT_PRIO) __builtin_amdgcn_s_setprio(0);
     };
     // V^T fragment of MFMA uu / d-tile dt: keys of the P registers 8uu..8uu+7 of this lane half
     auto vfrag = [&](const unsigned char* vb_, int kt, int uu, int dt) -> frag {
@@ -416,147 +407,294 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_partial(Args<T, D> A) {
       }
     };
 
-    // softmax of one sub-tile's scores (in place) -> bf16/fp32 probabilities pf; updates the
-    // running max (lazy rescale of o and l) and the running sum l
-    // kfirst: index in the unit's key list of the sub-tile's first key
-    auto softmax = [&](f32x16 (&sacc)[TPW], int kvalid, int kfirst, frag (&pf)[TPW][32 / KS]) {
+    // The pending PV product: V^T fragments and probabilities of the previous sub-tile. They start
+    // at zero, so the first sub-tile's "previous" product adds nothing.
+    frag va[NDT][NUU];
+    frag pf[NUU];
 #pragma unroll
-      for (int t = 0; t < TPW; ++t) {
-        if (kvalid < 32) {
+    for (int uu = 0; uu < NUU; ++uu) {
+      if constexpr (EPL == 8) {
 #pragma unroll
-          for (int j = 0; j < 16; ++j)
-            if (8 * (j >> 2) + 4 * hh2 + (j & 3) >= kvalid) sacc[t][j] = -INFINITY;
-        }
-        if constexpr (CAUSAL) {
-          if (kfirst + 32 > P) {  // the sub-tile reaches the block rows: mask j > s
-            const int srow = ((wave * TPW + t) * QT + l32) / G;
+        for (int i = 0; i < 8; ++i) pf[uu][i] = (bf16)0.f;
+      } else {
+        pf[uu] = 0.f;
+      }
 #pragma unroll
-            for (int j = 0; j < 16; ++j)
-              if (kfirst + 8 * (j >> 2) + 4 * hh2 + (j & 3) - P > srow) sacc[t][j] = -INFINITY;
-          }
-        }
-        float mx = fmaxf(fmaxf(sacc[t][0], sacc[t][1]), sacc[t][2]);
+      for (int dt = 0; dt < NDT; ++dt) va[dt][uu] = pf[uu];
+    }
+    // MFMA i of the pending PV product; consecutive ones go to different accumulators
+    auto pv_mma = [&](auto i) {
+      constexpr int I = decltype(i)::value, dt = I % NDT, uu = I / NDT;
+      o[dt] = MF::mma(va[dt][uu], pf[uu], o[dt]);
+    };
+    // MFMA i of the scores of one sub-tile (one chain, from zero)
+    auto qk_mma = [&](const frag (&kf)[NQK], f32x16& acc, auto i) {
+      constexpr int I = decltype(i)::value;
+      if constexpr (I == 0) {
+        f32x16 z;
 #pragma unroll
-        for (int j = 3; j < 15; j += 2) mx = fmaxf(fmaxf(mx, sacc[t][j]), sacc[t][j + 1]);
-        mx = fmaxf(mx, sacc[t][15]);
-        mx = fmaxf(mx, tt_swap_halves(mx));
-        // Lazy rescale: the reference max only moves when a row's max grows by more than
-        // 2^8 in the exponent; exponentials stay <= 256 and the final normalisation is exact.
-        if (__ballot((mx - mrun[t]) * A.c > RESCALE_LOG2)) {
-          const float mnew = fmaxf(mrun[t], mx);
-          // 0 on the first update; 1 for a row that has seen no visible key yet (causal), where
-          // both maxima are -inf and their difference would be NaN
-          const float alpha = (CAUSAL && mnew == -INFINITY) ? 1.f : tt_exp2((mrun[t] - mnew) * A.c);
-          lrun[t] *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) o[t][dt][j] *= alpha;
-          mrun[t] = mnew;
-        }
-        // (causal: a row may have no visible key yet in this piece; its probabilities are 0)
-        const float mc = (CAUSAL && mrun[t] == -INFINITY) ? 0.f : mrun[t] * A.c;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) sacc[t][j] = tt_exp2(fmaf(sacc[t][j], A.c, -mc));
-#pragma unroll
-        for (int uu = 0; uu < 32 / KS; ++uu) pf[t][uu] = MF::pfrag(sacc[t], uu);
-        // row sum of the probabilities exactly as the PV product uses them
-        lrun[t] = MF::psum(pf[t], sacc[t], lrun[t]);
+        for (int j = 0; j < 16; ++j) z[j] = 0.f;
+        acc = MF::mma(kf[0], qf[0], z);
+      } else {
+        acc = MF::mma(kf[I], qf[I], acc);
       }
     };
-    auto vread = [&](const unsigned char* vb_, int kt, frag (&va)[D / 32][32 / KS]) {
+    // Score register j of lane half h holds key 8(j/4) + 4h + j%4 of the sub-tile. Keys past the
+    // piece end, and (causal) block rows after the query's own block position, get -inf.
+    const int h4 = 4 * hh2;
+    auto mask = [&](f32x16& s, int kvalid, int kfirst) {
+      const int climit = (CAUSAL ? row / G + P - kfirst : 0);  // causal: keys above it are hidden
+      int h4o = h4;
+      asm volatile("" : "+v"(h4o));  // opaque here: the 16 key indices are not kept across steps
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int uu = 0; uu < 32 / KS; ++uu) va[dt][uu] = vfrag(vb_, kt, uu, dt);
-    };
-    auto pv = [&](const frag (&va)[D / 32][32 / KS], const frag (&pf)[TPW][32 / KS]) {
-      if (TT_AT_PRIO) __builtin_amdgcn_s_setprio(2);
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int uu = 0; uu < 32 / KS; ++uu)
-#pragma unroll
-          for (int t = 0; t < TPW; ++t) o[t][dt] = MF::mma(va[dt][uu], pf[t][uu], o[t][dt]);
-      if (TT_AT_PRIO) __builtin_amdgcn_s_setprio(0);
+      for (int j = 0; j < 16; ++j) {
+        const int c = 8 * (j >> 2) + (j & 3);
+        if (h4o + c >= kvalid) s[j] = -INFINITY;
+        if constexpr (CAUSAL) {
+          if (h4o + c > climit) s[j] = -INFINITY;
+        }
+      }
     };
 
+    const int nsub = (nkeys + 31) / 32;
     const int nst = (nkeys + KC - 1) / KC;
     tt_wait_vmem<0>();   // the previous piece's partial stores; the load counting below starts clean
-    __syncthreads();  // previous piece's readers are done with the ring
+    __syncthreads();     // previous piece's readers are done with the ring
 #pragma unroll
     for (int st = 0; st < PD; ++st)
       if (st < nst) issue_stage(st);
+    stage_ready(0, nst);
+    if (PD < nst) issue_stage(PD);
 
-    // one sub-tile: scores, softmax and the PV product
-    auto subtile = [&](int st, int kt) {
-      const int kvalid = nkeys - st * KC - kt * 32;  // keys of this sub-tile that exist
-      frag kf[D / KS];
-      kread(ring.k[st % NBUF], kt, kf);
-      f32x16 sacc[TPW];
-      qk(kf, sacc);
-      frag pf[TPW][32 / KS];
-      softmax(sacc, kvalid, ka + st * KC + kt * 32, pf);
-      frag va[D / 32][32 / KS];
-      vread(ring.v[st % NBUF], kt, va);
-      pv(va, pf);
-    };
-    for (int st = 0; st < nst; ++st) {
-      stage_ready(st, nst);                       // B_st
-      if (st + PD < nst) issue_stage(st + PD);    // into the buffer of stage st - 1
-      if (!active) continue;
+    // Row max of sub-tile j (after its masking), with the pending PV MFMAs issued between its
+    // steps when with_pv is set; then the lazy rescale. Returns the sub-tile's exponent offset.
+    auto row_max = [&](f32x16& sc, int j, auto with_pv) -> float {
+      const int kvalid = nkeys - 32 * j;
+      const int kfirst = ka + 32 * j;  // index in the unit's key list of the sub-tile's first key
+      if (kvalid < 32 || (CAUSAL && kfirst + 32 > P)) mask(sc, kvalid, kfirst);
+      float mx = -INFINITY;
+      auto vmax = [&](auto e) { mx = fmaxf(mx, sc[decltype(e)::value]); };
+      if constexpr (decltype(with_pv)::value) tt_interleave<NPV, 16, 0>(pv_mma, vmax, [](auto) {});
+      else tt_static_for<16>(vmax);
+      mx = tt_max_halves(mx);
+      // Lazy rescale: the reference max only moves when a row's max grows by more than
+      // 2^8 in the exponent; exponentials stay <= 256 and the final normalisation is exact.
+      if (__ballot((mx - mrun) * A.c > RESCALE_LOG2)) {
+        const float mnew = fmaxf(mrun, mx);
+        // 0 on the first update; 1 for a row that has seen no visible key yet (causal), where
+        // both maxima are -inf and their difference would be NaN
+        const float alpha = (CAUSAL && mnew == -INFINITY) ? 1.f : tt_exp2((mrun - mnew) * A.c);
+        lrun *= alpha;
 #pragma unroll
-      for (int kt = 0; kt < SPS; ++kt)
-        if (nkeys - st * KC - kt * 32 > 0) subtile(st, kt);
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int q = 0; q < 16; ++q) o[dt][q] *= alpha;
+        mrun = mnew;
+      }
+      // (causal: a row may have no visible key yet in this piece; its probabilities are 0)
+      return (CAUSAL && mrun == -INFINITY) ? 0.f : mrun * A.c;
+    };
+    // Exponentials of a sub-tile (scores sc, exponent offset mc) into the P^T operand and the row
+    // sum, with its V^T reads (vld(l): fragment l) and, when with_qk is set, the score MFMAs of the
+    // next sub-tile (K fragments kf, into sn) issued between their steps.
+    auto expo = [&](f32x16& sc, float mc, auto with_qk, const frag (&kf)[NQK], f32x16& sn, auto&& vld) {
+      float ps = 0.f;  // fp32: the sub-tile's row sum, added to lrun at the end
+      // each pair of bf16 probabilities goes to the row sum exactly as the PV product uses it
+      auto vexp = [&](auto e) {
+        constexpr int E = decltype(e)::value;
+        sc[E] = tt_exp2(fmaf(sc[E], A.c, -mc));
+        if constexpr (EPL == 8) {
+          if constexpr (E % 2 == 1) {
+            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+            const bf16x2 one = {(bf16)1.f, (bf16)1.f};
+            bf16x2 pr;
+            pr[0] = (bf16)sc[E - 1];
+            pr[1] = (bf16)sc[E];
+            pf[E / 8][E % 8 - 1] = pr[0];
+            pf[E / 8][E % 8] = pr[1];
+            lrun = __builtin_amdgcn_fdot2_f32_bf16(pr, one, lrun, false);
+          }
+        } else {
+          pf[E] = sc[E];  // fp32: score register E is the P^T operand of MFMA E
+          ps += sc[E];
+        }
+      };
+      if constexpr (decltype(with_qk)::value) {
+        tt_interleave<NQK, 16, NPV>([&](auto i) { qk_mma(kf, sn, i); }, vexp, vld);
+      } else {
+        tt_static_for<16>(vexp);
+        tt_static_for<NPV>(vld);
+      }
+      if constexpr (EPL != 8) lrun += ps;
+    };
+
+    f32x16 sa, sb;
+    if constexpr (PIPE) {
+      // Stage loads of the bf16 path with compile-time ring slot BUF: fast stages from the
+      // piece's context rows through one scalar base per stage, others through issue_chunk.
+      const unsigned char* kpiece = tt_uniform(reinterpret_cast<const unsigned char*>(kctx) + (size_t)ka * RB);
+      const unsigned char* vpiece = tt_uniform(reinterpret_cast<const unsigned char*>(vctx) + (size_t)ka * RB);
+      auto issue_stage_c = [&](auto buf, int st) {
+        constexpr int BUF = decltype(buf)::value;
+        if (ka + st * KC + KC <= fast_end) {
+          const unsigned char* sk = kpiece + (size_t)st * KC * RB;
+          const unsigned char* sv = vpiece + (size_t)st * KC * RB;
+          if constexpr (CPW == 2) {  // head_dim 128: two K and two V chunks, one asm block
+            tt_dma16x4_snt<BUF * GE::STAGE, BUF * GE::STAGE + 1024, (NBUF + BUF) * GE::STAGE,
+                           (NBUF + BUF) * GE::STAGE + 1024>(dkoff[0], dkoff[1], dvoff[0], dvoff[1], sk,
+                                                             sv, lds_k0);
+          } else {
+            tt_static_for<CPW>([&](auto c) {
+              constexpr int C = decltype(c)::value;
+              tt_dma16_snt<BUF * GE::STAGE + C * 1024>(dkoff[C], sk, lds_k0);
+              tt_dma16_snt<(NBUF + BUF) * GE::STAGE + C * 1024>(dvoff[C], sv, lds_k0);
+            });
+          }
+        } else {
+          issue_stage(st);
+        }
+      };
+      // K fragments of sub-tile KT of ring slot BUF
+      auto kread_c = [&](auto buf, auto kt, frag (&kf)[NQK]) {
+        constexpr int OFF = decltype(buf)::value * GE::STAGE + decltype(kt)::value * 32 * RB;
+#pragma unroll
+        for (int ks = 0; ks < NQK; ++ks)
+          kf[ks] = *reinterpret_cast<__attribute__((address_space(3))) const frag*>(koff[ks] + OFF);
+      };
+      // V^T fragment l (d tile l % NDT, MFMA l / NDT) of sub-tile KT of ring slot BUF: two
+      // transposing reads (see vfrag)
+      auto vread_c = [&](auto buf, auto kt, auto l) {
+        constexpr int L = decltype(l)::value, dt = L % NDT, uu = L / NDT;
+        constexpr int OFF = decltype(buf)::value * GE::STAGE + (decltype(kt)::value * 32 + 16 * uu) * RB;
+        typedef short s16x4 __attribute__((ext_vector_type(4)));
+        frag f;
+#pragma unroll
+        for (int rd = 0; rd < 2; ++rd) {
+          s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              reinterpret_cast<__attribute__((address_space(3))) s16x4*>(
+                  const_cast<__attribute__((address_space(3))) unsigned char*>(voff[dt] + OFF + 8 * rd * RB)));
+          bf16x4 y = __builtin_bit_cast(bf16x4, x);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) f[4 * rd + e] = y[e];
+        }
+        va[dt][uu] = f;
+      };
+
+      // Software pipeline over the piece's 32-key sub-tiles. Step j holds the scores of sub-tile
+      // j (sc) and the pending PV product of sub-tile j - 1; it
+      //   reads the K fragments of sub-tile j + 1 (after the barrier that makes its stage
+      //   resident), issues the PV MFMAs of sub-tile j - 1 with the row max of sub-tile j between
+      //   them, rescales (rarely), then issues the score MFMAs of sub-tile j + 1 (into sn) with
+      //   the exponentials and the V^T reads of sub-tile j between them.
+      // The last step's score MFMAs read a stale ring slot; those scores are never used. K is
+      // read one sub-tile ahead of V, so at a barrier two stages are in use. The loop runs NPH
+      // steps per iteration (one turn of the ring), so ring slots and sub-tile offsets are
+      // compile-time constants and every LDS address is a register plus an immediate.
+      constexpr int NPH = NBUF * SPS;
+      if (active) {
+        frag kf[NQK];
+        kread_c(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, kf);
+        tt_static_for<NQK>([&](auto i) { qk_mma(kf, sa, i); });
+      }
+      auto step = [&](auto ph, auto act, int j, f32x16& sc, f32x16& sn) {
+        constexpr int PH = decltype(ph)::value, PN = PH + 1;
+        constexpr int BUF = (PH / SPS) % NBUF, KT = PH % SPS;
+        constexpr int BUFN = (PN / SPS) % NBUF, KTN = PN % SPS;
+        const int jn = j + 1;
+        if constexpr (KTN == 0) {
+          if (jn < nsub) {  // sub-tile j + 1 opens a stage: make it resident
+            const int stn = jn / SPS;
+            stage_ready(stn, nst);  // every wave is done with stage stn - 2
+            if (stn + PD < nst) issue_stage_c(std::integral_constant<int, (BUFN + PD) % NBUF>{}, stn + PD);
+          }
+        }
+        if constexpr (!decltype(act)::value) return;  // a wave without query rows: loads only
+        frag kf[NQK];
+        kread_c(std::integral_constant<int, BUFN>{}, std::integral_constant<int, KTN>{}, kf);
+        const float mc = row_max(sc, j, std::true_type{});
+        expo(sc, mc, std::true_type{}, kf, sn, [&](auto l) {
+          vread_c(std::integral_constant<int, BUF>{}, std::integral_constant<int, KT>{}, l);
+        });
+      };
+      auto run = [&](auto act) {
+        for (int j0 = 0; j0 < nsub; j0 += NPH) {
+          tt_static_for<NPH>([&](auto ph) {
+            constexpr int PH = decltype(ph)::value;
+            if (j0 + PH < nsub) {
+              if constexpr (PH % 2 == 0) step(ph, act, j0 + PH, sa, sb);
+              else step(ph, act, j0 + PH, sb, sa);
+            }
+          });
+        }
+      };
+      if (active) run(std::true_type{});
+      else run(std::false_type{});
+      if (active) tt_static_for<NPV>(pv_mma);  // the last sub-tile's PV product
+    } else {
+      // One sub-tile after the other: scores, softmax, PV product.
+      for (int j = 0; j < nsub; ++j) {
+        if (j > 0 && j % SPS == 0) {
+          stage_ready(j / SPS, nst);
+          if (j / SPS + PD < nst) issue_stage(j / SPS + PD);
+        }
+        if (!active) continue;
+        frag kf[NQK];
+        kread(ring.k[(j / SPS) % NBUF], j % SPS, kf);
+        tt_static_for<NQK>([&](auto i) { qk_mma(kf, sa, i); });
+        const float mc = row_max(sa, j, std::false_type{});
+        const unsigned char* vst = ring.v[(j / SPS) % NBUF];
+        const int kt = j % SPS;
+        expo(sa, mc, std::false_type{}, kf, sb, [&](auto l) {
+          constexpr int L = decltype(l)::value, dt = L % NDT, uu = L / NDT;
+          va[dt][uu] = vfrag(vst, kt, uu, dt);
+        });
+        tt_static_for<NPV>(pv_mma);
+      }
     }
 
     // ---- epilogue: direct normalised output, or a normalised partial in slot w + u
     if (active) {
       const size_t slot = (size_t)w + u;
+      const float ltot = lrun + tt_shfl_xor(lrun, 32);
+      if (row < R) {
+        if (whole) {
+          const int s = row / G, hq = g * G + row % G;
+          T* op = A.out + (((size_t)bb * A.S + s) * A.Hq + hq) * D;
+          const float inv = 1.f / ltot;
 #pragma unroll
-      for (int t = 0; t < TPW; ++t) {
-        const float ltot = lrun[t] + tt_shfl_xor(lrun[t], 32);
-        const int row = (wave * TPW + t) * QT + l32;
-        if (row < R) {
-          if (whole) {
-            const int s = row / G, hq = g * G + row % G;
-            T* op = A.out + (((size_t)bb * A.S + s) * A.Hq + hq) * D;
-            const float inv = 1.f / ltot;
+          for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt)
+            for (int jg = 0; jg < 4; ++jg) {
+              const int d = dt * 32 + 8 * jg + 4 * hh2;
+              if constexpr (sizeof(T) == 2) {
+                bf16x4 v;
 #pragma unroll
-              for (int jg = 0; jg < 4; ++jg) {
-                const int d = dt * 32 + 8 * jg + 4 * hh2;
-                if constexpr (sizeof(T) == 2) {
-                  bf16x4 v;
+                for (int e = 0; e < 4; ++e) v[e] = (bf16)(o[dt][4 * jg + e] * inv);
+                *reinterpret_cast<bf16x4*>(op + d) = v;
+              } else {
+                f32x4 v;
 #pragma unroll
-                  for (int e = 0; e < 4; ++e) v[e] = (bf16)(o[t][dt][4 * jg + e] * inv);
-                  *reinterpret_cast<bf16x4*>(op + d) = v;
-                } else {
-                  f32x4 v;
-#pragma unroll
-                  for (int e = 0; e < 4; ++e) v[e] = o[t][dt][4 * jg + e] * inv;
-                  *reinterpret_cast<f32x4*>(op + d) = v;
-                }
+                for (int e = 0; e < 4; ++e) v[e] = o[dt][4 * jg + e] * inv;
+                *reinterpret_cast<f32x4*>(op + d) = v;
               }
-          } else {
-            typedef PartT<T> PT;
-            typedef PT pvec __attribute__((ext_vector_type(4)));
-            PT* wp = A.ws_o + (slot * R + row) * D;
-            // (causal: a row with no visible key in this piece leaves an empty partial)
-            const float inv = (CAUSAL && ltot == 0.f) ? 0.f : 1.f / ltot;
+            }
+        } else {
+          typedef PartT<T> PT;
+          typedef PT pvec __attribute__((ext_vector_type(4)));
+          PT* wp = A.ws_o + (slot * R + row) * D;
+          // (causal: a row with no visible key in this piece leaves an empty partial)
+          const float inv = (CAUSAL && ltot == 0.f) ? 0.f : 1.f / ltot;
 #pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt)
+          for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-              for (int jg = 0; jg < 4; ++jg) {
-                const int d = dt * 32 + 8 * jg + 4 * hh2;
-                pvec v;
+            for (int jg = 0; jg < 4; ++jg) {
+              const int d = dt * 32 + 8 * jg + 4 * hh2;
+              pvec v;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = (PT)(o[t][dt][4 * jg + e] * inv);
-                *reinterpret_cast<pvec*>(wp + d) = v;
-              }
-            if (hh2 == 0) A.ws_ml[slot * R + row] = make_float2(mrun[t], ltot);
-          }
+              for (int e = 0; e < 4; ++e) v[e] = (PT)(o[dt][4 * jg + e] * inv);
+              *reinterpret_cast<pvec*>(wp + d) = v;
+            }
+          if (hh2 == 0) A.ws_ml[slot * R + row] = make_float2(mrun, ltot);
         }
       }
     }
