@@ -175,7 +175,12 @@ struct Args {
   const int32_t* ctx_start;
   const int32_t* ctx_len;
   T* out;
-  PartT<T>* ws_o;  // [slots][R][D]: normalised partial output O / l
+  // [slots][ceil(R/32)][D/8][2][32][4]: normalised partial output O / l in the MFMA output
+  // layout of the wave that owns each 32-row tile (element (row, d) of a slot at
+  // ((((row/32) D/8 + d/8) 2 + (d/4)%2) 32 + row%32) 4 + d%4). Each partial store instruction
+  // then writes 1 KiB and each wave 32 contiguous KiB, spread over all memory channels; the
+  // combine's read of one 4-element quad of consecutive rows is contiguous as well.
+  PartT<T>* ws_o;
   float2* ws_ml;   // [slots][R]: (running max of the raw scores m, sum l relative to m)
   int B, S, Hq, Hkv;
   int64_t ctx_rows;
@@ -681,18 +686,17 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_partial(Args<T, D> A) {
         } else {
           typedef PartT<T> PT;
           typedef PT pvec __attribute__((ext_vector_type(4)));
-          PT* wp = A.ws_o + (slot * R + row) * D;
+          PT* wp = A.ws_o + ((slot * ((R + 31) / 32) + wave) * (D / 8) * 64 + lane) * 4;
           // (causal: a row with no visible key in this piece leaves an empty partial)
           const float inv = (CAUSAL && ltot == 0.f) ? 0.f : 1.f / ltot;
 #pragma unroll
           for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
             for (int jg = 0; jg < 4; ++jg) {
-              const int d = dt * 32 + 8 * jg + 4 * hh2;
               pvec v;
 #pragma unroll
               for (int e = 0; e < 4; ++e) v[e] = (PT)(o[dt][4 * jg + e] * inv);
-              *reinterpret_cast<pvec*>(wp + d) = v;
+              *reinterpret_cast<pvec*>(wp + (dt * 4 + jg) * 256) = v;
             }
           if (hh2 == 0) A.ws_ml[slot * R + row] = make_float2(mrun, ltot);
         }
@@ -727,24 +731,30 @@ __device__ __forceinline__ void block_sum2(int64_t& a, int64_t& b) {
 }
 
 // Split-K merge of a unit's normalised partials: O = sum_k e^(m_k - M) l_k Ohat_k /
-// sum_k e^(m_k - M) l_k. Workgroup = RPB query rows of one unit; thread (row rr, group sg, part
-// tr) owns VPT consecutive output elements of its row and the partials of workgroups wf + sg,
-// wf + sg + NSG, ... (CB loads in flight together); the NSG groups of a row are merged in the
-// order sg = 0, 1, ... through LDS, a fixed order, so the result is reproducible. Many partials
-// per unit (long sequences) use several groups per row, few partials several rows per group.
+// sum_k e^(m_k - M) l_k. Workgroup = CB_RB query rows x QB quads (4 consecutive output elements)
+// of one unit, rows fastest, so the 16-byte partial loads of consecutive threads are contiguous; thread (row rr, quad qq, group sg) owns one quad of its row and the
+// partials of workgroups wf + sg, wf + sg + NSG, ... (CB loads in flight together); the NSG
+// groups of a row are merged in the order sg = 0, 1, ... through LDS, a fixed order, so the
+// result is reproducible. Many partials per unit (long sequences) use several groups per quad.
+constexpr int CB_RB = 16;
 template <typename T, int D, int NSG>
 __global__ __launch_bounds__(CB_THREADS) void attn_combine(Args<T, D> A) {
   typedef PartT<T> PT;
   constexpr int VPT = 16 / (int)sizeof(PT);  // elements per thread (one 16-byte load)
-  constexpr int TPR = D / VPT;               // threads per row part
-  constexpr int RPB = CB_THREADS / (TPR * NSG);  // rows per workgroup
-  static_assert(RPB >= 1 && RPB * TPR * NSG == CB_THREADS, "combine geometry");
+  static_assert(VPT == 4, "fp32 partials, read one 4-element quad per thread");
+  constexpr int NQ = D / VPT;                // quads per row
+  constexpr int QB = CB_THREADS / (CB_RB * NSG);  // quads per workgroup
+  static_assert(QB >= 1 && QB * CB_RB * NSG == CB_THREADS && NQ % QB == 0, "combine geometry");
   constexpr int CB = 8;                      // partials per group whose loads are in flight together
   const int G = A.Hq / A.Hkv;
   const int R = A.S * G;
-  const int u = blockIdx.x;    // unit on x (up to B * Hkv workgroups), row block on y
-  const int rr = threadIdx.x / (TPR * NSG);
-  const int row = blockIdx.y * RPB + rr;
+  const int u = blockIdx.x;    // unit on x (up to B * Hkv workgroups), row block on y, quads on z
+  const int rr = threadIdx.x % CB_RB;
+  const int qq = (threadIdx.x / CB_RB) % QB;
+  const int sg = threadIdx.x / (CB_RB * QB);
+  const int row = blockIdx.y * CB_RB + rr;
+  const int quad = blockIdx.z * QB + qq;
+  const int RW = (R + 31) / 32;  // 32-row tiles of the partials
   const int bb = u / A.Hkv, g = u - bb * A.Hkv;
   // key-space offsets: sum of N_b' = ctx_len[b'] + S over b' < bb, and over all b'
   int64_t before = 0, total = 0;
@@ -759,9 +769,8 @@ __global__ __launch_bounds__(CB_THREADS) void attn_combine(Args<T, D> A) {
   const int64_t Ou = (int64_t)A.Hkv * before + (int64_t)g * N;
   const int wf = owner_of(Ou, Ttot, A.W), wl = owner_of(Ou + N - 1, Ttot, A.W);
   if (wf == wl) return;  // one workgroup held the whole unit and wrote the output itself
-  const int sg = (threadIdx.x / TPR) % NSG, tr = threadIdx.x % TPR;
   const bool live = row < R;
-  const int d = tr * VPT;
+  const int d = quad * VPT;
   float M = -INFINITY, L = 0.f;
   float acc[VPT];
 #pragma unroll
@@ -775,7 +784,8 @@ __global__ __launch_bounds__(CB_THREADS) void attn_combine(Args<T, D> A) {
       const size_t slot = (size_t)wk + u;
       if (wk <= wl) {
         ml[k] = A.ws_ml[slot * R + row];
-        ov[k] = *reinterpret_cast<const u32x4*>(A.ws_o + (slot * R + row) * D + d);
+        ov[k] = *reinterpret_cast<const u32x4*>(
+            A.ws_o + ((((slot * RW + row / 32) * (D / 8) + quad / 2) * 2 + quad % 2) * 32 + row % 32) * VPT);
       } else {
         ml[k] = make_float2(-INFINITY, 0.f);
         ov[k] = u32x4{0u, 0u, 0u, 0u};
@@ -799,23 +809,23 @@ __global__ __launch_bounds__(CB_THREADS) void attn_combine(Args<T, D> A) {
     M = bm;
   }
   if constexpr (NSG > 1) {
-    __shared__ float gm[RPB][NSG][TPR], gl[RPB][NSG][TPR];
-    __shared__ float ga[RPB][NSG][TPR][VPT];
-    gm[rr][sg][tr] = M;
-    gl[rr][sg][tr] = L;
+    __shared__ float gm[CB_RB][NSG][QB], gl[CB_RB][NSG][QB];
+    __shared__ float ga[CB_RB][NSG][QB][VPT];
+    gm[rr][sg][qq] = M;
+    gl[rr][sg][qq] = L;
 #pragma unroll
-    for (int e = 0; e < VPT; ++e) ga[rr][sg][tr][e] = acc[e];
+    for (int e = 0; e < VPT; ++e) ga[rr][sg][qq][e] = acc[e];
     __syncthreads();
     if (sg != 0) return;
     for (int q = 1; q < NSG; ++q) {
-      const float m2 = gm[rr][q][tr];
+      const float m2 = gm[rr][q][qq];
       if (m2 == -INFINITY) continue;
       const float bm = fmaxf(M, m2);
       const float r1 = (M == -INFINITY) ? 0.f : tt_exp2((M - bm) * A.c);
       const float r2 = tt_exp2((m2 - bm) * A.c);
-      L = L * r1 + gl[rr][q][tr] * r2;
+      L = L * r1 + gl[rr][q][qq] * r2;
 #pragma unroll
-      for (int e = 0; e < VPT; ++e) acc[e] = acc[e] * r1 + ga[rr][q][tr][e] * r2;
+      for (int e = 0; e < VPT; ++e) acc[e] = acc[e] * r1 + ga[rr][q][qq][e] * r2;
       M = bm;
     }
   }
@@ -848,7 +858,8 @@ int launch(const void* q, const void* kb, const void* vb, const void* kc, const 
   int W = (int)std::min<int64_t>((int64_t)AT_TARGET_WG, (tmax + MIN_KEYS_PER_WG - 1) / MIN_KEYS_PER_WG);
   if (W < 1) W = 1;
   const size_t slots = (size_t)W + U;
-  const size_t o_bytes = tt_align_up(slots * R * D * sizeof(PartT<T>), 256);
+  // partial rows are stored in whole 32-row tiles
+  const size_t o_bytes = tt_align_up(slots * (size_t)((R + 31) / 32 * 32) * D * sizeof(PartT<T>), 256);
   const size_t need = o_bytes + tt_align_up(slots * R * sizeof(float2), 256);
   int st = tt_workspace_check(ws, ws_bytes, need);
   if (st != 0) return st < 0 ? st : TT_OK;
@@ -864,15 +875,18 @@ int launch(const void* q, const void* kb, const void* vb, const void* kc, const 
   hipLaunchKernelGGL((attn_partial<T, D, CAUSAL>), dim3(W), dim3(AT_THREADS), 0, stream, a);
   if (tt_launch_status() != TT_OK) return TT_ERR_HIP;
   if (W > 1) {
-    // slot groups per row: enough to cover a unit's partials (about W / U + 1) in one batch
-    constexpr int TPR = D / (16 / (int)sizeof(PartT<T>));
-    constexpr int NSG_MAX = CB_THREADS / TPR;
+    // slot groups per quad: enough to cover a unit's partials (about W / U + 1) in one batch
+    constexpr int NQ = D / (16 / (int)sizeof(PartT<T>));
+    constexpr int NSG_MAX = 4;
+    const int rblocks = (R + CB_RB - 1) / CB_RB;
     if (W / U + 1 >= 16) {
-      hipLaunchKernelGGL((attn_combine<T, D, NSG_MAX>), dim3(U, R), dim3(CB_THREADS), 0, stream, a);
-    } else {
-      constexpr int RPB = CB_THREADS / TPR;
-      hipLaunchKernelGGL((attn_combine<T, D, 1>), dim3(U, (R + RPB - 1) / RPB), dim3(CB_THREADS), 0,
+      constexpr int QB = CB_THREADS / (CB_RB * NSG_MAX);
+      hipLaunchKernelGGL((attn_combine<T, D, NSG_MAX>), dim3(U, rblocks, NQ / QB), dim3(CB_THREADS), 0,
                          stream, a);
+    } else {
+      constexpr int QB = CB_THREADS / CB_RB;
+      hipLaunchKernelGGL((attn_combine<T, D, 1>), dim3(U, rblocks, NQ / QB), dim3(CB_THREADS), 0, stream,
+                         a);
     }
     if (tt_launch_status() != TT_OK) return TT_ERR_HIP;
   }

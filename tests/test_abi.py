@@ -48,7 +48,8 @@ def _attn(**kw):
 def test_attn_workspace_query_and_size():
     st, n = _attn()
     assert st == 0
-    # 2 units, 4128 keys -> ceil(4128/128) = 33 workgroups; slots = 33 + 2, R = 256 rows, D = 128
+    # 2 units, 4128 keys -> ceil(4128/128) = 33 workgroups; slots = 33 + 2, R = 256 rows (whole
+    # 32-row tiles), D = 128
     # fp32 normalised partials + (m, l) as two fp32 per row
     slots, R, D = 35, 256, 128
     expect = -(-(slots * R * D * 4) // 256) * 256 + -(-(slots * R * 8) // 256) * 256
