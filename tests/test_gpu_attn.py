@@ -124,3 +124,25 @@ def test_extreme_scores_exercise_running_max():
     ref = oracle.block_attention(inp, wl.dtype)
     assert np.all(np.isfinite(got))
     assert float(np.max(np.abs(got - ref))) <= ATOL_BF16
+
+
+def test_growing_scores_rescale_at_many_steps():
+    """Context keys scaled by a factor that grows from 1 to 8 along the prefix: each row's max
+    keeps rising by more than 2^8 in the exponent every few 32-key sub-tiles, so the lazy rescale
+    fires at many positions of the pipelined sub-tile loop (all 8 steps of a ring turn) and in
+    pieces that straddle units. A rescale applied to the wrong PV product, or skipped, overflows
+    or mis-weights the output. V is halved (exact) so |o| stays below 4."""
+    wl = _wl(1, B=2, prefixes=[3000, 1100])
+    wl.wid = 611
+    inp = synth.attn_inputs(wl)
+    kc = oracle.decode(inp["k_ctx"], "bf16").astype(np.float32)
+    for b in range(wl.B):
+        a, n = int(inp["ctx_start"][b]), int(inp["ctx_len"][b])
+        kc[:, a:a + n] *= (1.0 + 7.0 * np.arange(n, dtype=np.float32) / n)[None, :, None]
+    inp["k_ctx"] = synth.to_bf16_bits(kc)
+    for k in ("v_blk", "v_ctx"):
+        inp[k] = synth.to_bf16_bits(oracle.decode(inp[k], "bf16").astype(np.float32) * 0.5)
+    got = _run(inp, wl)
+    ref = oracle.block_attention(inp, wl.dtype)
+    assert np.all(np.isfinite(got))
+    assert float(np.max(np.abs(got - ref))) <= ATOL_BF16
