@@ -857,6 +857,10 @@ int launch(const void* q, const void* kb, const void* vb, const void* kc, const 
   const int64_t tmax = (int64_t)U * ((int64_t)max_prefix + S);
   int W = (int)std::min<int64_t>((int64_t)AT_TARGET_WG, (tmax + MIN_KEYS_PER_WG - 1) / MIN_KEYS_PER_WG);
   if (W < 1) W = 1;
+  // A multiple of the unit count: with equal sequence lengths every unit then starts at a
+  // workgroup boundary, and no workgroup pays a second piece's loads and partial store (batch 1,
+  // 2K prefix: 33 -> 32 workgroups, 15.8 -> 14.1 us). Ragged lengths keep the exact balance.
+  if (W > U) W -= W % U;
   const size_t slots = (size_t)W + U;
   // partial rows are stored in whole 32-row tiles
   const size_t o_bytes = tt_align_up(slots * (size_t)((R + 31) / 32 * 32) * D * sizeof(PartT<T>), 256);

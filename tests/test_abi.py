@@ -48,10 +48,10 @@ def _attn(**kw):
 def test_attn_workspace_query_and_size():
     st, n = _attn()
     assert st == 0
-    # 2 units, 4128 keys -> ceil(4128/128) = 33 workgroups; slots = 33 + 2, R = 256 rows (whole
-    # 32-row tiles), D = 128
+    # 2 units, 4128 keys -> ceil(4128/128) = 33 workgroups, rounded down to a multiple of the unit
+    # count: 32; slots = 32 + 2, R = 256 rows (whole 32-row tiles), D = 128
     # fp32 normalised partials + (m, l) as two fp32 per row
-    slots, R, D = 35, 256, 128
+    slots, R, D = 34, 256, 128
     expect = -(-(slots * R * D * 4) // 256) * 256 + -(-(slots * R * 8) // 256) * 256
     assert n == expect
     st, n4 = _attn(B=4, max_prefix=131072, ctx_rows=4 * 131072)

@@ -28,10 +28,13 @@ def _run(inp, wl):
 
 
 def _splits_inside_a_block(wl):
-    """Whether the launch's key split (256 workgroups at most, 128 keys each at least, key lists
-    of all (sequence, kv head) units end to end) cuts some unit inside its last S keys."""
+    """Whether the launch's key split (256 workgroups at most, 128 keys each at least, a multiple
+    of the unit count when there are more workgroups than units, key lists of all (sequence, kv
+    head) units end to end) cuts some unit inside its last S keys."""
     U = wl.B * wl.Hkv
     W = max(1, min(256, -(-U * (wl.max_prefix + wl.S) // 128)))
+    if W > U:
+        W -= W % U
     lens = [p + wl.S for p in wl.prefixes]
     T = wl.Hkv * sum(lens)
     starts, acc = [], 0
