@@ -13,20 +13,20 @@
 // both) at every boundary.
 //
 // Inside a workgroup (8 waves, one 32-row query tile each): K/V stages of KC keys go straight from
-// HBM into an LDS ring of NBUF stages (direct global->LDS loads, three stages in flight) and are
-// shared by all S*G query rows (up to 256), so every key byte is read from HBM once. Scores are
-// computed transposed, S^T = K Q^T, on 32x32 MFMA tiles: the result layout gives each lane one
-// query row (column lane%32) and 16 keys, so the row max and sum need one cross-half exchange
-// only. The exponentials are written back into the same registers and used directly as the B
-// operand of O^T = V^T P^T; the V^T operand is read from the row-major V stage with transposing
-// LDS reads, in the key order of the score registers.
+// HBM into an LDS ring of NBUF stages (direct global->LDS loads) and are shared by all S*G query
+// rows (up to 256), so every key byte is read from HBM once. Scores are computed transposed,
+// S^T = K Q^T, on 32x32 MFMA tiles: the result layout gives each lane one query row (column
+// lane%32) and 16 keys, so the row max and sum need one cross-half exchange only. The
+// exponentials are written back into the same registers and used directly as the B operand of
+// O^T = V^T P^T; the V^T operand is read from the row-major V stage with transposing LDS reads,
+// in the key order of the score registers.
 //
-// What bounds it (MI355X counters at 4 x 131072 keys): the LDS pipe, active about 94% of the
-// kernel's time. Each of the 8 waves reads the whole K and V of every stage (8 KiB each per 32
-// keys; the V^T reads are 64-bit transposing reads, so V costs twice K's instructions). Two
-// query tiles per wave halve that traffic but leave one wave per SIMD and, as compiled, move the
-// output accumulators between register files every sub-tile: slower. Issuing the second
-// sub-tile's score MFMAs before the first one's softmax did not change the time either.
+// The bf16 sub-tile loop is software-pipelined (a wave's softmax arithmetic runs between its own
+// MFMAs) and unrolled over one turn of the ring, so that every LDS address is a register plus an
+// immediate: with two waves per SIMD, each instruction a wave issues costs it an issue slot, and
+// removing the per-sub-tile address and M0 arithmetic is what shortened the kernel (MI355X
+// counters at 4 x 131072 keys: 22% fewer instructions, 13% fewer cycles). The schedule alone,
+// without the unroll, did not change the time.
 #include "common.h"
 
 namespace {

@@ -135,36 +135,22 @@ __device__ __forceinline__ uint32_t tt_lds_addr(const void* p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)TT_LDS_PTR(const void, p));
 }
 
-// Direct global->LDS load of 16 bytes per lane: lane i's bytes land at LDS address base + 16 i.
-// Written as inline asm on purpose: the compiler then does not track these writes to LDS, so it
-// does not put a wait for every outstanding global load in front of each LDS read of a ring
-// that such loads fill. Ordering is the caller's job instead: each stage's readers wait (counted
-// vmcnt, then a barrier) for that stage's loads only, and a buffer is refilled only after the
-// barrier that ends its reads. M0 (which holds the LDS base) is saved to a scratch SGPR and
+// Direct global->LDS load of 16 bytes per lane (lane i's bytes land at LDS address base + 16 i),
+// with the non-temporal cache policy, for data read exactly once (a streamed KV cache or weight
+// matrix): on MI355X a stream of these reaches about 7.1 TB/s from HBM against 6.1 TB/s without
+// the policy. Written as inline asm on purpose: the compiler then does not track these writes to
+// LDS, so it does not put a wait for every outstanding global load in front of each LDS read of
+// a ring that such loads fill. Ordering is the caller's job instead: each stage's readers wait
+// (counted vmcnt, then a barrier) for that stage's loads only, and a buffer is refilled only after
+// the barrier that ends its reads. M0 (which holds the LDS base) is saved to a scratch SGPR and
 // restored inside the same asm, so the compiler's own use of M0 is unaffected. The only register
 // output is that scratch SGPR, written by a scalar move; the load returns nothing to registers.
-__device__ __forceinline__ void tt_dma16(const void* gptr, uint32_t lds_base) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"  // one wait state between an SALU write of M0 and its use by an LDS DMA
-      "global_load_lds_dwordx4 %1, off\n\t"
-      "s_nop 0\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(gptr), "s"(lds_base)
-      : "memory");
-}
-
-// The same with the non-temporal cache policy, for data read exactly once (a streamed KV cache):
-// on MI355X a stream of these reaches about 7.1 TB/s from HBM against 6.1 TB/s without it.
 __device__ __forceinline__ void tt_dma16_nt(const void* gptr, uint32_t lds_base) {
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
+      "s_nop 0\n\t"  // one wait state between an SALU write of M0 and its use by an LDS DMA
       "global_load_lds_dwordx4 %1, off nt\n\t"
       "s_nop 0\n\t"
       "s_mov_b32 m0, %0"
@@ -175,7 +161,7 @@ __device__ __forceinline__ void tt_dma16_nt(const void* gptr, uint32_t lds_base)
 
 // Direct global->LDS load (non-temporal) from a wave-uniform base plus a per-lane 32-bit byte
 // offset (the scalar-base form of the instruction), into LDS at lds_base + OFF + 16 lane. M0 is
-// saved and restored inside the asm as in tt_dma16.
+// saved and restored inside the asm as in tt_dma16_nt.
 template <int OFF>
 __device__ __forceinline__ void tt_dma16_snt(uint32_t voff, const void* sbase, uint32_t lds_base) {
   uint32_t saved;
