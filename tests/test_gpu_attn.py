@@ -146,3 +146,30 @@ def test_growing_scores_rescale_at_many_steps():
     ref = oracle.block_attention(inp, wl.dtype)
     assert np.all(np.isfinite(got))
     assert float(np.max(np.abs(got - ref))) <= ATOL_BF16
+
+
+def _sweep_cases(n=24, seed=2024):
+    """Seeded random shapes: batch 1-5, block size 1-16, grouped heads with S*G <= 256, head_dim
+    64 or 128, prefixes from 0 to 3000 (so pieces start and end anywhere in the unrolled loop's
+    ring turn, and workgroups take one or several pieces)."""
+    g = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        D = int(g.choice([64, 128]))
+        Hkv = int(g.choice([1, 2, 3, 4]))
+        G = int(g.choice([1, 2, 4, 8, 16]))
+        S = int(g.integers(1, 17))
+        if S * G > 256:
+            continue
+        B = int(g.integers(1, 6))
+        pref = [int(x) for x in g.integers(0, 3001, size=B)]
+        cases.append((B, S, Hkv * G, Hkv, D, pref))
+    return cases
+
+
+@pytest.mark.parametrize("case", _sweep_cases())
+def test_random_shape_sweep(case):
+    B, S, Hq, Hkv, D, pref = case
+    wl = _wl(1, B=B, S=S, Hq=Hq, Hkv=Hkv, D=D, prefixes=pref)
+    wl.wid = 800 + (sum(pref) + 31 * S + Hq) % 997
+    _full_check(wl)
