@@ -1,7 +1,7 @@
 // Denoiser block attention ("Nemotron-Labs-TwoTower" wiki page, section "Architecture").
 //
 // A "unit" is one (sequence b, kv head g). Its key list is [k_ctx rows of b ; the S block rows],
-// N_b = ctx_len[b] + S keys, and its query tile is the S*G rows (block position s, grouped head hh)
+// N_b = len_b + S keys (len_b = ctx_len[b] within the bounds of ctx_rows_of), and its query tile is the S*G rows (block position s, grouped head hh)
 // that share kv head g (G = Hq/Hkv; the grouping is contiguous: query head h uses kv head h/G).
 //
 // Work split (flash-decoding with stream-K balance): the key lists of all units, laid end to end,
@@ -112,15 +112,31 @@ struct alignas(16) Ring {
 
 template <int NT>
 struct Scan {
-  int pb[AT_MAX_B + 1];  // pb[b] = sum_{b' < b} (ctx_len[b'] + S)
+  int pb[AT_MAX_B + 1];  // pb[b] = sum_{b' < b} (len_b' + S)
   int tmp[NT];
 };
 
-// Exclusive prefix sums of N_b = ctx_len[b] + S into sc.pb[0..B] (B <= AT_MAX_B), NT threads:
+// The context rows [start, start + len) of sequence b that every kernel here uses: ctx_start[b]
+// clamped to [0, ctx_rows], ctx_len[b] to [0, min(max_prefix, ctx_rows - start)]. Inside the
+// caller's contract these are the values given. Outside it no access leaves k_ctx / v_ctx and the
+// key-space sums stay within the bound the host checked (B Hkv (max_prefix + S) < 2^31).
+struct CtxRows {
+  int64_t start;
+  int len;
+};
+__device__ __forceinline__ CtxRows ctx_rows_of(const int32_t* cs, const int32_t* cl, int b, int64_t ctx_rows,
+                                               int max_prefix) {
+  const int64_t st = min(max((int64_t)cs[b], (int64_t)0), ctx_rows);
+  const int64_t cap = min((int64_t)max_prefix, ctx_rows - st);
+  return CtxRows{st, (int)min(max((int64_t)cl[b], (int64_t)0), cap)};
+}
+
+// Exclusive prefix sums of N_b = len_b + S (len_b from ctx_rows_of) into sc.pb[0..B] (B <= AT_MAX_B), NT threads:
 // thread t sums its PER consecutive lengths, a shuffle scan runs inside each wave, and the wave
 // totals are added through LDS (two barriers).
 template <int NT>
-__device__ void scan_lengths(Scan<NT>& sc, const int32_t* __restrict__ ctx_len, int B, int S) {
+__device__ void scan_lengths(Scan<NT>& sc, const int32_t* __restrict__ ctx_start, const int32_t* __restrict__ ctx_len,
+                             int B, int S, int64_t ctx_rows, int max_prefix) {
   const int t = threadIdx.x;
   constexpr int PER = AT_MAX_B / NT;
   constexpr int NW = NT / TT_WAVE;
@@ -130,7 +146,7 @@ __device__ void scan_lengths(Scan<NT>& sc, const int32_t* __restrict__ ctx_len, 
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
     int b = t * PER + k;
-    v[k] = (b < B) ? ctx_len[b] + S : 0;
+    v[k] = (b < B) ? ctx_rows_of(ctx_start, ctx_len, b, ctx_rows, max_prefix).len + S : 0;
     loc += v[k];
   }
   const int lane = t & (TT_WAVE - 1), wv = t / TT_WAVE;
@@ -184,6 +200,7 @@ struct Args {
   float2* ws_ml;   // [slots][R]: (running max of the raw scores m, sum l relative to m)
   int B, S, Hq, Hkv;
   int64_t ctx_rows;
+  int max_prefix;
   int W;
   float c;  // softmax_scale * log2(e)
 };
@@ -223,7 +240,7 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_partial(Args<T, D> A) {
   const int U = A.B * A.Hkv;
   const bool active = wave * QT < R;  // this wave owns query rows [32 wave, 32 wave + 32)
 
-  scan_lengths<AT_THREADS>(sc, A.ctx_len, A.B, A.S);
+  scan_lengths<AT_THREADS>(sc, A.ctx_start, A.ctx_len, A.B, A.S, A.ctx_rows, A.max_prefix);
   const int64_t Ttot = (int64_t)A.Hkv * sc.pb[A.B];
   const int64_t lo = (int64_t)w * Ttot / A.W;
   const int64_t hi = (int64_t)(w + 1) * Ttot / A.W;
@@ -281,8 +298,9 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_partial(Args<T, D> A) {
     const int ke = (int)min((int64_t)N, hi - Ou);
     const bool whole = (ka == 0 && ke == N);
     const int P = N - A.S;
-    const T* kctx = A.kc + ((size_t)g * A.ctx_rows + A.ctx_start[bb]) * D;  // row 0 of this unit
-    const T* vctx = A.vc + ((size_t)g * A.ctx_rows + A.ctx_start[bb]) * D;
+    const int64_t cst = ctx_rows_of(A.ctx_start, A.ctx_len, bb, A.ctx_rows, A.max_prefix).start;
+    const T* kctx = A.kc + ((size_t)g * A.ctx_rows + cst) * D;  // row 0 of this unit
+    const T* vctx = A.vc + ((size_t)g * A.ctx_rows + cst) * D;
     const size_t blk_stride = (size_t)A.Hkv * D;                             // between block rows
     const T* kblk = A.kb + ((size_t)bb * A.S * A.Hkv + g) * D;
     const T* vblk = A.vb + ((size_t)bb * A.S * A.Hkv + g) * D;
@@ -756,16 +774,16 @@ __global__ __launch_bounds__(CB_THREADS) void attn_combine(Args<T, D> A) {
   const int quad = blockIdx.z * QB + qq;
   const int RW = (R + 31) / 32;  // 32-row tiles of the partials
   const int bb = u / A.Hkv, g = u - bb * A.Hkv;
-  // key-space offsets: sum of N_b' = ctx_len[b'] + S over b' < bb, and over all b'
+  // key-space offsets: sum of N_b' = len_b' + S over b' < bb, and over all b'
   int64_t before = 0, total = 0;
   for (int b2 = threadIdx.x; b2 < A.B; b2 += CB_THREADS) {
-    const int64_t n = (int64_t)A.ctx_len[b2] + A.S;
+    const int64_t n = (int64_t)ctx_rows_of(A.ctx_start, A.ctx_len, b2, A.ctx_rows, A.max_prefix).len + A.S;
     total += n;
     if (b2 < bb) before += n;
   }
   block_sum2(before, total);
   const int64_t Ttot = (int64_t)A.Hkv * total;
-  const int N = A.ctx_len[bb] + A.S;
+  const int N = ctx_rows_of(A.ctx_start, A.ctx_len, bb, A.ctx_rows, A.max_prefix).len + A.S;
   const int64_t Ou = (int64_t)A.Hkv * before + (int64_t)g * N;
   const int wf = owner_of(Ou, Ttot, A.W), wl = owner_of(Ou + N - 1, Ttot, A.W);
   if (wf == wl) return;  // one workgroup held the whole unit and wrote the output itself
@@ -874,7 +892,7 @@ int launch(const void* q, const void* kb, const void* vb, const void* kc, const 
   a.ctx_start = cs; a.ctx_len = cl; a.out = (T*)out;
   a.ws_o = (PartT<T>*)ws;
   a.ws_ml = (float2*)((char*)ws + o_bytes);
-  a.B = B; a.S = S; a.Hq = Hq; a.Hkv = Hkv; a.ctx_rows = ctx_rows; a.W = W;
+  a.B = B; a.S = S; a.Hq = Hq; a.Hkv = Hkv; a.ctx_rows = ctx_rows; a.max_prefix = max_prefix; a.W = W;
   a.c = scale * LOG2E;
   hipLaunchKernelGGL((attn_partial<T, D, CAUSAL>), dim3(W), dim3(AT_THREADS), 0, stream, a);
   if (tt_launch_status() != TT_OK) return TT_ERR_HIP;
@@ -930,7 +948,9 @@ int attn_dispatch(const void* q, const void* k_blk, const void* v_blk, const voi
 }
 
 // Appends the block's K/V rows to the cache and advances ctx_len: one workgroup per sequence b,
-// 16-byte copies; every thread reads ctx_len[b] before the barrier, thread 0 updates it after.
+// 16-byte copies; every thread reads ctx_len[b] before the barrier, thread 0 updates it after. A
+// sequence outside the caller's contract (negative start or length, length above max_prefix, or
+// no room for S rows before ctx_rows) is left as it is: nothing written, ctx_len[b] unchanged.
 constexpr int AP_THREADS = 256;
 __global__ __launch_bounds__(AP_THREADS) void kv_append(const unsigned char* __restrict__ k_new,
                                                         const unsigned char* __restrict__ v_new,
@@ -938,9 +958,11 @@ __global__ __launch_bounds__(AP_THREADS) void kv_append(const unsigned char* __r
                                                         unsigned char* __restrict__ v_ctx,
                                                         const int32_t* __restrict__ ctx_start,
                                                         int32_t* __restrict__ ctx_len, int S, int Hkv,
-                                                        int row_bytes, int64_t ctx_rows) {
+                                                        int row_bytes, int64_t ctx_rows, int max_prefix) {
   const int b = blockIdx.x;
-  const int64_t r0 = (int64_t)ctx_start[b] + ctx_len[b];  // first new cache row of sequence b
+  const int32_t c0 = ctx_start[b], l0 = ctx_len[b];
+  const int64_t r0 = (int64_t)c0 + l0;  // first new cache row of sequence b
+  if (c0 < 0 || l0 < 0 || l0 > max_prefix || r0 + S > ctx_rows) return;  // the same for the workgroup
   const int gpr = row_bytes / 16;                          // 16-byte granules per row
   const int n = S * Hkv * gpr;
   for (int x = threadIdx.x; x < n; x += AP_THREADS) {
@@ -952,7 +974,7 @@ __global__ __launch_bounds__(AP_THREADS) void kv_append(const unsigned char* __r
     *reinterpret_cast<u32x4*>(v_ctx + dst) = *reinterpret_cast<const u32x4*>(v_new + src);
   }
   __syncthreads();
-  if (threadIdx.x == 0) ctx_len[b] = ctx_len[b] + S;
+  if (threadIdx.x == 0) ctx_len[b] = l0 + S;
 }
 
 }  // namespace
@@ -985,6 +1007,6 @@ extern "C" int tt_context_extend(const void* q, const void* k_new, const void* v
   const int row_bytes = D * (dtype == TT_BF16 ? 2 : 4);
   hipLaunchKernelGGL(kv_append, dim3(B), dim3(AP_THREADS), 0, s, (const unsigned char*)k_new,
                      (const unsigned char*)v_new, (unsigned char*)k_ctx, (unsigned char*)v_ctx, ctx_start, ctx_len,
-                     S, Hkv, row_bytes, ctx_rows);
+                     S, Hkv, row_bytes, ctx_rows, max_prefix);
   return tt_launch_status();
 }

@@ -69,8 +69,12 @@ enum tt_status {
  *   k_blk, v_blk [B][S][Hkv][D]
  *   k_ctx, v_ctx [Hkv][ctx_rows][D]   (sequences packed along ctx_rows)
  *   ctx_start, ctx_len  int32 [B] on the device; ctx_len[b] may be 0.
- * Caller's contract (not checked): 0 <= ctx_len[b] <= max_prefix and
- *   ctx_start[b] + ctx_len[b] <= ctx_rows. max_prefix sizes the launch.
+ * Caller's contract: 0 <= ctx_start[b], 0 <= ctx_len[b] <= max_prefix and
+ *   ctx_start[b] + ctx_len[b] <= ctx_rows. max_prefix sizes the launch. The kernels read both
+ *   arrays through a clamp, in every build: start = ctx_start[b] within [0, ctx_rows], then
+ *   len = ctx_len[b] within [0, min(max_prefix, ctx_rows - start)], and the output is the
+ *   attention over those rows. Inside the contract this changes nothing; outside it no access
+ *   leaves k_ctx / v_ctx.
  * Supported: D in {64, 128}; S*(Hq/Hkv) <= 256; dtype TT_F32 or TT_BF16.
  * Errors: TT_ERR_ARG for null pointers, B/S/Hq/Hkv <= 0, Hq % Hkv != 0, ctx_rows < 0,
  *   max_prefix < 0, max_prefix > 0 with null k_ctx/v_ctx, non-finite or non-positive scale;
@@ -100,9 +104,12 @@ int tt_block_attn(const void* q, const void* k_blk, const void* v_blk,
  * of kv head g receives k_new[b][j][g] (and v_new likewise), and ctx_len[b] += S.
  *
  * Layouts as tt_block_attn (k_new, v_new in the place of k_blk, v_blk); k_ctx, v_ctx and
- * ctx_len are updated in place. Caller's contract (not checked): ctx_len[b] <= max_prefix, and
- * the S rows after each sequence's cached rows are inside [0, ctx_rows) and belong to it (no
- * other sequence's rows there). Sizes, dtypes and limits as tt_block_attn.
+ * ctx_len are updated in place. Caller's contract: that of tt_block_attn, and the S rows after
+ * each sequence's cached rows are inside [0, ctx_rows) and belong to it (no other sequence's rows
+ * there). The attention reads the lengths through the clamp of tt_block_attn. A sequence with
+ * ctx_start[b] < 0, ctx_len[b] outside [0, max_prefix] or ctx_start[b] + ctx_len[b] + S > ctx_rows
+ * gets no append: its cache rows and ctx_len[b] are left unchanged. Sizes, dtypes and limits as
+ * tt_block_attn.
  * Errors: those of tt_block_attn; TT_ERR_ARG also for a null k_ctx / v_ctx, and when
  *   max_prefix + S > ctx_rows (no room to append).
  * Workspace: as tt_block_attn for the same arguments.

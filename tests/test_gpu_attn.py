@@ -173,3 +173,40 @@ def test_random_shape_sweep(case):
     wl = _wl(1, B=B, S=S, Hq=Hq, Hkv=Hkv, D=D, prefixes=pref)
     wl.wid = 800 + (sum(pref) + 31 * S + Hq) % 997
     _full_check(wl)
+
+
+def _clamped(start, length, ctx_rows, max_prefix):
+    """The rows the call attends to for lengths outside the caller's contract (include/tt.h):
+    start within [0, ctx_rows], then length within [0, min(max_prefix, ctx_rows - start)]."""
+    st = np.clip(np.asarray(start, dtype=np.int64), 0, ctx_rows)
+    cap = np.minimum(max_prefix, ctx_rows - st)
+    ln = np.clip(np.asarray(length, dtype=np.int64), 0, cap)
+    return st.astype(np.int32), ln.astype(np.int32)
+
+
+def test_lengths_outside_the_contract_are_clamped():
+    """Every way out of the contract at once, beside one sequence inside it: a length above
+    max_prefix, a negative length, a negative start, rows past ctx_rows, a start past ctx_rows.
+    The output is the attention over the clamped rows, read within the cache."""
+    wl = _wl(1, B=6, prefixes=[200, 50, 120, 80, 30, 64])
+    wl.wid = 911
+    inp = synth.attn_inputs(wl)
+    R = inp["k_ctx"].shape[1]
+    assert R == 544
+    max_prefix = 150
+    start = np.array([0, 200, -40, 500, 600, 480], dtype=np.int32)
+    length = np.array([200, -5, 120, 80, 7, 64], dtype=np.int32)
+    inp["ctx_start"], inp["ctx_len"] = start, length
+    d = attn_dev(inp)
+    got = bmd.tt_block_attn(d["q"], d["k_blk"], d["v_blk"], d["k_ctx"], d["v_ctx"], d["ctx_start"],
+                            d["ctx_len"], max_prefix=max_prefix, softmax_scale=d["scale"])
+    torch.cuda.synchronize()
+    got = got.float().cpu().numpy().astype(np.float64)
+    st, ln = _clamped(start, length, R, max_prefix)
+    assert st.tolist() == [0, 200, 0, 500, 544, 480] and ln.tolist() == [150, 0, 120, 44, 0, 64]
+    ref = oracle.block_attention(dict(inp, ctx_start=st, ctx_len=ln), wl.dtype)
+    err = float(np.max(np.abs(got - ref)))
+    assert err <= ATOL_BF16, err
+    # the arrays themselves are inputs only
+    assert np.array_equal(d["ctx_start"].cpu().numpy(), start)
+    assert np.array_equal(d["ctx_len"].cpu().numpy(), length)

@@ -151,3 +151,33 @@ def test_deterministic():
     a = _run(inp, wl)[0]
     b = _run(inp, wl)[0]
     assert np.array_equal(a, b)
+
+
+def test_sequences_outside_the_contract_get_no_append():
+    """One sequence inside the contract, one with ctx_len above max_prefix, one whose S new rows
+    would pass ctx_rows: the attention reads the clamped rows (start within [0, ctx_rows], length
+    within [0, min(max_prefix, ctx_rows - start)]); only the first sequence is appended to."""
+    wl = synth.workload(1, B=3, prefixes=[100, 60, 40])
+    wl.wid = 912
+    inp = synth.context_inputs(wl)
+    R = inp["k_ctx"].shape[1]
+    assert R == 248 and list(inp["ctx_start"]) == [0, 116, 192]
+    start = np.array([0, 116, 200], dtype=np.int32)
+    length = np.array([100, 120, 40], dtype=np.int32)
+    inp["ctx_start"], inp["ctx_len"] = start, length
+    got, kc, vc, ln = _run(inp, wl)  # max_prefix = 100
+    st = np.clip(start.astype(np.int64), 0, R)
+    lc = np.clip(length.astype(np.int64), 0, np.minimum(wl.max_prefix, R - st))
+    assert lc.tolist() == [100, 100, 40]
+    clamped = dict(inp, ctx_start=st.astype(np.int32), ctx_len=lc.astype(np.int32))
+    rows = [(b, s, h) for b in range(wl.B) for s in range(wl.S) for h in range(wl.Hq)]
+    ref = oracle.context_extend(clamped, wl.dtype, rows=rows)
+    err = max(float(np.max(np.abs(got[r] - ref[r]))) for r in rows)
+    assert err <= ATOL_BF16, err
+    # the cache as given, with sequence 0's S new rows written after its 100 cached rows
+    ekc, evc = np.array(inp["k_ctx"], copy=True), np.array(inp["v_ctx"], copy=True)
+    for j in range(wl.S):
+        ekc[:, 100 + j] = inp["k_blk"][0, j]
+        evc[:, 100 + j] = inp["v_blk"][0, j]
+    assert np.array_equal(kc, ekc) and np.array_equal(vc, evc)
+    assert ln.tolist() == [116, 120, 40]
