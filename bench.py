@@ -108,6 +108,11 @@ def cpu_baseline(wl, host, steps):
         blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # noqa: BLE001
         blas_threads = 1
+    try:
+        blas = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        blas_name = f"{blas.get('name', '?')} {blas.get('version', '')}".strip()
+    except Exception:  # noqa: BLE001
+        blas_name = "unknown"
     S = wl.S
     layers = []
     for inp in host["attn"]:
@@ -126,7 +131,7 @@ def cpu_baseline(wl, host, steps):
     return {"value": steps / dt, "unit": "block-steps/s", "cores": int(blas_threads), "kind": "oracle",
             "sample": f"{steps} block-steps of sequence 0 (all {len(layers)} attention layer(s), "
                       f"{S} LM-head rows, unmask) with numpy fp64; host has {os.cpu_count()} CPUs, "
-                      f"BLAS threads {blas_threads}",
+                      f"BLAS {blas_name}, {blas_threads} threads",
             "seconds": dt}
 
 
