@@ -497,10 +497,23 @@ int lm_direct(const void* h, const void* w, float* o, int M, int H, int V, hipSt
   return lm_launch<bf16, MT, BMT, VT, STEP, RING, KCH>(h, w, o, M, H, V, s);
 }
 
+// Up to 16 rows: the vocabulary tile follows V. The widest tile (64 VT rows per wave) that still
+// gives 512 workgroups (two per compute unit) is taken, else the narrowest. That keeps a small
+// vocabulary, such as one GPU's shard of a split LM head, spread over the chip. Measured at
+// H = 2688: V = 16384 runs in 31.6 us with VT = 1 against 44.3 us with VT = 4, V = 32768 in 36.2
+// against 46.8 us, and V = 131072 stays with VT = 4 (106.8 against 118.2 us with VT = 1). Every
+// logit is the same chain of MFMAs for any VT, so the values do not depend on the choice.
+int lm_lds16(const void* h, const void* w, float* o, int M, int H, int V, hipStream_t s) {
+  constexpr int TV = LM_WAVES * lds_cols_per_part<TT_LM_LDS16>();  // vocabulary rows per workgroup
+  if ((V + TV - 1) / TV >= 512) return lm_try_lds<TT_LM_LDS16>(h, w, o, M, H, V, s);
+  if ((V + 127) / 128 >= 512) return lm_try_lds<16, 1, 2, 64, true, 4>(h, w, o, M, H, V, s);
+  return lm_try_lds<16, 1, 1, 64, true, 4>(h, w, o, M, H, V, s);
+}
+
 int lm_bf16(const void* h, const void* w, float* o, int M, int H, int V, hipStream_t s) {
   if (M > 16 && H % TT_GEMM_KB == 0) return tt_lm_gemm_launch(h, w, o, M, H, V, s);
   int st = 1;
-  if (M <= 16) st = lm_try_lds<TT_LM_LDS16>(h, w, o, M, H, V, s);
+  if (M <= 16) st = lm_lds16(h, w, o, M, H, V, s);
   if (st != 1) return st;
   if (M <= 32) return lm_direct<TT_LM_CFG32>(h, w, o, M, H, V, s);
   if (M <= 64) return lm_direct<TT_LM_CFG64>(h, w, o, M, H, V, s);

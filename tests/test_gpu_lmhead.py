@@ -32,7 +32,11 @@ def _bound(inp, dtype):
                                          (128, 2688, 2048, "bf16"), (64, 2688, 2304, "bf16"),
                                          (512, 2688, 1024, "bf16"), (100, 288, 777, "bf16"), (1, 32, 256, "bf16"),
                                          (7, 256, 1001, "bf16"), (24, 256, 1000, "bf16"), (65, 128, 513, "bf16"),
-                                         (16, 96, 2000, "bf16"), (130, 2688, 700, "bf16")])
+                                         (16, 96, 2000, "bf16"), (130, 2688, 700, "bf16"),
+                                         # up to 16 rows the vocabulary tile follows V: 64, 128, 256
+                                         # rows per workgroup (one GPU's shard of an 8-way split first)
+                                         (16, 2688, 16384, "bf16"), (16, 256, 70001, "bf16"),
+                                         (9, 128, 131000, "bf16")])
 def test_full_compare(M, H, V, dtype):
     wl = synth.workload(1, B=1, H=H, V=V, dtype=dtype)
     wl.B, wl.S = 1, M
