@@ -484,37 +484,48 @@ constexpr int lds_cols_per_part() { return VT * Shape<bf16, MT>::NV; }
 #define TT_LM_CFGBIG 32, 4, 2, 32, 8, 256
 #endif
 
-// Runs the LDS-staged kernel when the stage width divides H; returns 1 when it does not apply.
-template <int MT, int BMT, int VT, int KW, bool NT, int NSET>
-int lm_try_lds(const void* h, const void* w, float* o, int M, int H, int V, hipStream_t s) {
-  if (H % KW != 0) return 1;
-  return lm_lds_launch<MT, BMT, VT, KW, NT, NSET>(h, w, o, M, H, V, s);
-}
-
 template <int MT, int BMT, int VT, int STEP, int RING, int KCH>
 int lm_direct(const void* h, const void* w, float* o, int M, int H, int V, hipStream_t s) {
   if (H % STEP != 0) return lm_launch<bf16, MT, BMT, VT, 32, RING * STEP / 32, KCH>(h, w, o, M, H, V, s);
   return lm_launch<bf16, MT, BMT, VT, STEP, RING, KCH>(h, w, o, M, H, V, s);
 }
 
-// Up to 16 rows: the vocabulary tile follows V. The widest tile (64 VT rows per wave) that still
-// gives 512 workgroups (two per compute unit) is taken, else the narrowest. That keeps a small
-// vocabulary, such as one GPU's shard of a split LM head, spread over the chip. Measured at
-// H = 2688: V = 16384 runs in 31.6 us with VT = 1 against 44.3 us with VT = 4, V = 32768 in 36.2
-// against 46.8 us, and V = 131072 stays with VT = 4 (106.8 against 118.2 us with VT = 1). Every
+// The LDS-staged kernel's vocabulary tile follows the grid: the widest tile (64 VT rows per wave,
+// VT = 4, 2, 1) whose vocabulary tiles times 16-row blocks still give 512 workgroups (two per
+// compute unit), else the narrowest. At V = 131072 and up to 16 rows that is VT = 4. A small
+// vocabulary, such as one GPU's shard of a split LM head, stays spread over the chip. Measured at
+// H = 2688, 16 rows: V = 16384 takes 31.6 us with VT = 1 against 44.3 us with VT = 4, V = 32768
+// 36.2 against 46.8 us; V = 131072 stays with VT = 4 (106.8 against 118.2 us with VT = 1). Every
 // logit is the same chain of MFMAs for any VT, so the values do not depend on the choice.
-int lm_lds16(const void* h, const void* w, float* o, int M, int H, int V, hipStream_t s) {
-  constexpr int TV = LM_WAVES * lds_cols_per_part<TT_LM_LDS16>();  // vocabulary rows per workgroup
-  if ((V + TV - 1) / TV >= 512) return lm_try_lds<TT_LM_LDS16>(h, w, o, M, H, V, s);
-  if ((V + 127) / 128 >= 512) return lm_try_lds<16, 1, 2, 64, true, 4>(h, w, o, M, H, V, s);
-  return lm_try_lds<16, 1, 1, 64, true, 4>(h, w, o, M, H, V, s);
+int lds_vt(int M, int V) {
+  const int nmb = (M + 15) / 16;
+  if ((int64_t)((V + 255) / 256) * nmb >= 512) return 4;
+  if ((int64_t)((V + 127) / 128) * nmb >= 512) return 2;
+  return 1;
+}
+
+// bf16 with H a multiple of the LDS stage: the LDS-staged kernel up to 16 rows, and up to 64 rows
+// when the GEMM kernel's 128 x 512 tiles would give 64 workgroups or fewer (V <= 32768). There a
+// workgroup's pass over H sets the GEMM's time whatever M (about 91 us at V = 16384 against
+// 32-37 us for the LDS-staged kernel at 32-64 rows; measured at H = 2688).
+bool lm_use_lds(int M, int H, int V) {
+  if (H % 64 != 0) return false;
+  return M <= 16 || (M <= 64 && (V + 511) / 512 <= 64);
+}
+
+template <bool RED>
+int lm_lds_by_vt(const void* h, const void* w, float* o, int M, int H, int V, hipStream_t s, TtRedArgs red) {
+  const int vt = lds_vt(M, V);
+  static_assert(LM_WAVES * lds_cols_per_part<TT_LM_LDS16>() == 256, "VT = 4 is the 256-row tile");
+  if (vt == 4) return lm_lds_launch<TT_LM_LDS16, RED>(h, w, o, M, H, V, s, red);
+  if (vt == 2) return lm_lds_launch<16, 1, 2, 64, true, 4, RED>(h, w, o, M, H, V, s, red);
+  return lm_lds_launch<16, 1, 1, 64, true, 4, RED>(h, w, o, M, H, V, s, red);
 }
 
 int lm_bf16(const void* h, const void* w, float* o, int M, int H, int V, hipStream_t s) {
+  const TtRedArgs none{nullptr, nullptr, -1, nullptr, 0};
+  if (lm_use_lds(M, H, V)) return lm_lds_by_vt<false>(h, w, o, M, H, V, s, none);
   if (M > 16 && H % TT_GEMM_KB == 0) return tt_lm_gemm_launch(h, w, o, M, H, V, s);
-  int st = 1;
-  if (M <= 16) st = lm_lds16(h, w, o, M, H, V, s);
-  if (st != 1) return st;
   if (M <= 32) return lm_direct<TT_LM_CFG32>(h, w, o, M, H, V, s);
   if (M <= 64) return lm_direct<TT_LM_CFG64>(h, w, o, M, H, V, s);
   return lm_direct<TT_LM_CFGBIG>(h, w, o, M, H, V, s);
@@ -523,15 +534,16 @@ int lm_bf16(const void* h, const void* w, float* o, int M, int H, int V, hipStre
 }  // namespace
 
 // Fused LM head + vocabulary reduction (bf16, H % 64 == 0): which kernel, and how many records per
-// row it writes. The same kernel and tile as the logits path for each M (so the accumulators are
-// the same): M <= 16 the LDS-staged kernel, larger M the GEMM kernel (128 columns per record).
+// row it writes. The same kernel as the logits path for each (M, V), so the accumulators are the
+// same: the LDS-staged kernel (16 VT columns per record) where lm_use_lds holds, else the GEMM
+// kernel (128 columns per record).
 int tt_lm_reduce_nparts(int M, int V) {
-  const int cols = M <= 16 ? lds_cols_per_part<TT_LM_LDS16>() : 128;
+  const int cols = lm_use_lds(M, 64, V) ? 16 * lds_vt(M, V) : 128;
   return (V + cols - 1) / cols;
 }
 
 int tt_lm_reduce_launch(const void* hidden, const void* w, int M, int H, int V, TtRedArgs red, hipStream_t s) {
-  if (M <= 16) return lm_lds_launch<TT_LM_LDS16, true>(hidden, w, nullptr, M, H, V, s, red);
+  if (lm_use_lds(M, H, V)) return lm_lds_by_vt<true>(hidden, w, nullptr, M, H, V, s, red);
   return tt_lm_gemm_reduce_launch(hidden, w, M, H, V, red, s);
 }
 

@@ -147,8 +147,15 @@ def test_fused_workspace_query():
         M = 16 * B
         st, n = _fu(B=B)
         assert st == 0 and n == M * (131072 // cols) * 16 + M * 16, (B, n)
+    # small vocabularies: the LDS-staged kernel's tile is 64 VT rows with 16 VT columns per
+    # record, VT the widest of 4, 2, 1 whose grid (vocabulary tiles x 16-row blocks) reaches 512;
+    # up to 64 rows it runs when V <= 32768
     st, n = _fu(V=1000)
-    assert st == 0 and n == 16 * 16 * 16 + 16 * 16      # ceil(1000 / 64) = 16 records per row
+    assert st == 0 and n == 16 * 63 * 16 + 16 * 16      # VT = 1: ceil(1000 / 16) = 63 records per row
+    st, n = _fu(B=4, V=16384)
+    assert st == 0 and n == 64 * 512 * 16 + 64 * 16     # VT = 2 (128 x 4 = 512 workgroups): 32 columns
+    st, n = _fu(B=5, V=16384)
+    assert st == 0 and n == 80 * 128 * 16 + 80 * 16     # 80 rows: the GEMM kernel, 128 columns
     assert _fu(ws=P, nbytes=10)[0] == _lib.TT_ERR_WORKSPACE
 
 

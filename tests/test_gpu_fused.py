@@ -80,7 +80,7 @@ def _steps(wl, steps, use_bias=True, gamma=None, inp=None):
 @pytest.mark.parametrize("B,S,H,V,mask_id", [
     (1, 16, 256, 4099, 3), (1, 7, 128, 1000, 999), (3, 16, 128, 1000, 0), (4, 16, 192, 2050, 64),
     (5, 16, 192, 3001, 127), (12, 13, 128, 2050, 128), (1, 64, 64, 300, 3), (2, 1, 64, 2, 1),
-    (3, 33, 64, 777, 5), (9, 16, 320, 1537, 3),
+    (3, 33, 64, 777, 5), (9, 16, 320, 1537, 3), (2, 16, 256, 16384, 3),
 ])
 def test_fused_against_oracle(B, S, H, V, mask_id):
     wl = _wl(B, S, H, V, mask_id)

@@ -36,7 +36,10 @@ def _bound(inp, dtype):
                                          # up to 16 rows the vocabulary tile follows V: 64, 128, 256
                                          # rows per workgroup (one GPU's shard of an 8-way split first)
                                          (16, 2688, 16384, "bf16"), (16, 256, 70001, "bf16"),
-                                         (9, 128, 131000, "bf16")])
+                                         (9, 128, 131000, "bf16"),
+                                         # 17-64 rows: the LDS-staged kernel while V <= 32768, else GEMM
+                                         (40, 256, 32768, "bf16"), (40, 256, 32769, "bf16"),
+                                         (64, 2688, 16384, "bf16")])
 def test_full_compare(M, H, V, dtype):
     wl = synth.workload(1, B=1, H=H, V=V, dtype=dtype)
     wl.B, wl.S = 1, M
