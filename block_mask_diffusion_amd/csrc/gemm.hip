@@ -1,4 +1,5 @@
-// LM-head product for more than 16 hidden rows ("Nemotron-Labs-TwoTower" wiki page, section
+// LM-head product for more than 16 hidden rows, bf16 (up to 64 rows on a vocabulary of 32768 or
+// less the LDS-staged kernel of lmhead.hip runs instead) ("Nemotron-Labs-TwoTower" wiki page, section
 // "Block-wise generation": every denoising step predicts all masked positions of every block in
 // parallel). Up to a hundred-odd rows the W stream from HBM sets the pace; from a few hundred
 // rows on, the matrix cores and the re-reads of the hidden rows from L2 do.

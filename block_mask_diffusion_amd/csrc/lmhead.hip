@@ -469,8 +469,9 @@ constexpr int lds_cols_per_part() { return VT * Shape<bf16, MT>::NV; }
 // Kernel choice (measured on MI355X at H = 2688, V = 131072): M <= 16 the LDS-staged kernel
 // <MT, BMT, VT, KW, NT, NSET>; larger M the MFMA GEMM kernel (gemm.hip), which with its
 // non-temporal W stream beats the LDS-staged kernel from 17 rows on (123 against 137 us at 64
-// rows); the direct kernel <MT, BMT, VT, STEP, RING, KCH> for fp32 and for H not a multiple of
-// the stage width.
+// rows) while its grid fills the chip (lm_use_lds below has the small-vocabulary exception);
+// the direct kernel <MT, BMT, VT, STEP, RING, KCH> for fp32 and for H not a multiple of the
+// stage width.
 #ifndef TT_LM_LDS16
 #define TT_LM_LDS16 16, 1, 4, 64, true, 4
 #endif
