@@ -1,5 +1,5 @@
-// LM-head product for more than 16 hidden rows, bf16 (up to 64 rows on a vocabulary of 32768 or
-// less the LDS-staged kernel of lmhead.hip runs instead) ("Nemotron-Labs-TwoTower" wiki page, section
+// LM-head product for more than 16 hidden rows, bf16 (on small vocabularies, up to 128 rows, the
+// LDS-staged kernel of lmhead.hip runs instead) ("Nemotron-Labs-TwoTower" wiki page, section
 // "Block-wise generation": every denoising step predicts all masked positions of every block in
 // parallel). Up to a hundred-odd rows the W stream from HBM sets the pace; from a few hundred
 // rows on, the matrix cores and the re-reads of the hidden rows from L2 do.
@@ -350,9 +350,14 @@ int gemm_launch(const void* hidden, const void* w, float* logits, int M, int H, 
 
 // Tile by M (measured at H = 2688, V = 131072): up to 128 hidden rows, 128 x 512 tiles (W read
 // once, few re-reads of the hidden rows); beyond, 256 x 256 (two hidden-row blocks share W in L2).
+// On a vocabulary of 32768 or less the 128 x 512 tiles give 64 workgroups or fewer, and the
+// 256 x 256 tile, with twice as many, is faster at any M (128 rows, V = 32768: 78.6 against
+// 94.7 us). Each output is the same chain of MFMAs in either tile.
+int gemm_wm(int M, int V) { return (M <= 128 && (V + 511) / 512 > 64) ? 1 : 2; }
+
 int tt_lm_gemm_launch(const void* hidden, const void* w, float* logits, int M, int H, int V, hipStream_t s) {
   const TtRedArgs none{nullptr, nullptr, -1, nullptr, 0};
-  if (M <= 128) return gemm_launch<1, false>(hidden, w, logits, M, H, V, none, s);
+  if (gemm_wm(M, V) == 1) return gemm_launch<1, false>(hidden, w, logits, M, H, V, none, s);
   return gemm_launch<2, false>(hidden, w, logits, M, H, V, none, s);
 }
 
@@ -360,6 +365,6 @@ int tt_lm_gemm_launch(const void* hidden, const void* w, float* logits, int M, i
 // must be ceil(V / 128).
 int tt_lm_gemm_reduce_launch(const void* hidden, const void* w, int M, int H, int V, TtRedArgs red,
                              hipStream_t s) {
-  if (M <= 128) return gemm_launch<1, true>(hidden, w, nullptr, M, H, V, red, s);
+  if (gemm_wm(M, V) == 1) return gemm_launch<1, true>(hidden, w, nullptr, M, H, V, red, s);
   return gemm_launch<2, true>(hidden, w, nullptr, M, H, V, red, s);
 }

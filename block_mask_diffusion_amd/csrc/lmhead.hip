@@ -505,13 +505,15 @@ int lds_vt(int M, int V) {
   return 1;
 }
 
-// bf16 with H a multiple of the LDS stage: the LDS-staged kernel up to 16 rows, and up to 64 rows
-// when the GEMM kernel's 128 x 512 tiles would give 64 workgroups or fewer (V <= 32768). There a
-// workgroup's pass over H sets the GEMM's time whatever M (about 91 us at V = 16384 against
-// 32-37 us for the LDS-staged kernel at 32-64 rows; measured at H = 2688).
+// bf16 with H a multiple of the LDS stage: the LDS-staged kernel up to 16 rows, and up to 128 rows
+// when the GEMM kernel's 128 x 512 tiles would give 64 workgroups or fewer (V <= 32768) and the
+// LDS-staged kernel's re-reads of W (one per 16 rows) stay small (V M <= 2^21). With so few
+// workgroups one workgroup's pass over H sets the GEMM's time whatever M: about 91 us at
+// V = 16384, against 32-37 us for the LDS-staged kernel at 32-64 rows and 63 us at 128 rows
+// (measured at H = 2688).
 bool lm_use_lds(int M, int H, int V) {
   if (H % 64 != 0) return false;
-  return M <= 16 || (M <= 64 && (V + 511) / 512 <= 64);
+  return M <= 16 || (M <= 128 && (V + 511) / 512 <= 64 && (int64_t)V * M <= (int64_t)1 << 21);
 }
 
 template <bool RED>

@@ -149,13 +149,17 @@ def test_fused_workspace_query():
         assert st == 0 and n == M * (131072 // cols) * 16 + M * 16, (B, n)
     # small vocabularies: the LDS-staged kernel's tile is 64 VT rows with 16 VT columns per
     # record, VT the widest of 4, 2, 1 whose grid (vocabulary tiles x 16-row blocks) reaches 512;
-    # up to 64 rows it runs when V <= 32768
+    # up to 128 rows it runs when V <= 32768 and V * rows <= 2^21
     st, n = _fu(V=1000)
     assert st == 0 and n == 16 * 63 * 16 + 16 * 16      # VT = 1: ceil(1000 / 16) = 63 records per row
     st, n = _fu(B=4, V=16384)
     assert st == 0 and n == 64 * 512 * 16 + 64 * 16     # VT = 2 (128 x 4 = 512 workgroups): 32 columns
-    st, n = _fu(B=5, V=16384)
-    assert st == 0 and n == 80 * 128 * 16 + 80 * 16     # 80 rows: the GEMM kernel, 128 columns
+    st, n = _fu(B=8, V=16384)
+    assert st == 0 and n == 128 * 256 * 16 + 128 * 16   # VT = 4 (64 x 8 = 512 workgroups): 64 columns
+    st, n = _fu(B=8, V=16385)
+    assert st == 0 and n == 128 * 129 * 16 + 128 * 16   # V * rows above 2^21: the GEMM kernel, 128 columns
+    st, n = _fu(B=9, V=16384)
+    assert st == 0 and n == 144 * 128 * 16 + 144 * 16   # 144 rows: the GEMM kernel
     assert _fu(ws=P, nbytes=10)[0] == _lib.TT_ERR_WORKSPACE
 
 

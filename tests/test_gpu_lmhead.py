@@ -37,9 +37,11 @@ def _bound(inp, dtype):
                                          # rows per workgroup (one GPU's shard of an 8-way split first)
                                          (16, 2688, 16384, "bf16"), (16, 256, 70001, "bf16"),
                                          (9, 128, 131000, "bf16"),
-                                         # 17-64 rows: the LDS-staged kernel while V <= 32768, else GEMM
+                                         # 17-128 rows: the LDS-staged kernel while V <= 32768 and
+                                         # V M <= 2^21; else the GEMM, its 256 x 256 tile while V <= 32768
                                          (40, 256, 32768, "bf16"), (40, 256, 32769, "bf16"),
-                                         (64, 2688, 16384, "bf16")])
+                                         (64, 2688, 16384, "bf16"), (128, 256, 16384, "bf16"),
+                                         (128, 256, 16385, "bf16"), (100, 256, 32769, "bf16")])
 def test_full_compare(M, H, V, dtype):
     wl = synth.workload(1, B=1, H=H, V=V, dtype=dtype)
     wl.B, wl.S = 1, M
