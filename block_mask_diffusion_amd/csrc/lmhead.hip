@@ -540,8 +540,8 @@ int lm_bf16(const void* h, const void* w, float* o, int M, int H, int V, hipStre
 // row it writes. The same kernel as the logits path for each (M, V), so the accumulators are the
 // same: the LDS-staged kernel (16 VT columns per record) where lm_use_lds holds, else the GEMM
 // kernel (128 columns per record).
-int tt_lm_reduce_nparts(int M, int V) {
-  const int cols = lm_use_lds(M, 64, V) ? 16 * lds_vt(M, V) : 128;
+int tt_lm_reduce_nparts(int M, int H, int V) {
+  const int cols = lm_use_lds(M, H, V) ? 16 * lds_vt(M, V) : 128;
   return (V + cols - 1) / cols;
 }
 

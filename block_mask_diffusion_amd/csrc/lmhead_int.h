@@ -21,6 +21,6 @@ __attribute__((visibility("hidden"))) int tt_lm_gemm_reduce_launch(const void* h
                                                                    hipStream_t s);
 
 // Fused LM head + vocabulary reduction (bf16, H % TT_GEMM_KB == 0): records per row, and launch.
-__attribute__((visibility("hidden"))) int tt_lm_reduce_nparts(int M, int V);
+__attribute__((visibility("hidden"))) int tt_lm_reduce_nparts(int M, int H, int V);
 __attribute__((visibility("hidden"))) int tt_lm_reduce_launch(const void* hidden, const void* w, int M, int H,
                                                               int V, TtRedArgs red, hipStream_t s);

@@ -316,7 +316,7 @@ extern "C" int tt_lmhead_unmask(const void* hidden, const void* w, const int32_t
   if (dtype != TT_BF16 || H % TT_GEMM_KB != 0 || S > 64) return TT_ERR_UNSUPPORTED;
   if ((size_t)B * S > (size_t)INT32_MAX) return TT_ERR_UNSUPPORTED;
   const int M = B * S;
-  const int nparts = tt_lm_reduce_nparts(M, V);
+  const int nparts = tt_lm_reduce_nparts(M, H, V);
   if ((size_t)M * nparts > (size_t)INT32_MAX) return TT_ERR_UNSUPPORTED;
   const size_t parts_bytes = (size_t)M * nparts * sizeof(Partial);
   const size_t need = parts_bytes + (size_t)M * sizeof(Partial);
