@@ -45,7 +45,61 @@ def parse():
     ap.add_argument("--cpu-steps", type=int, default=2, help="oracle block-steps in the CPU sample")
     ap.add_argument("--copy-calib", action="store_true",
                     help="run a 1 GiB device copy first (calibrates HBM byte counters)")
+    ap.add_argument("--share", action="store_true",
+                    help="instead of the step: time the kernels at one GPU's share of an 8-way split "
+                         "(LM head over a 16384-row vocabulary shard, attention over one kv head)")
     return ap.parse_args()
+
+
+def share(torch, bmd):
+    """One GPU's share of an 8-way split, timed on this GPU: the LM head over a 16384-row vocabulary
+    shard (H = 2688, 16 to 512 hidden rows) and attention over one kv head (16 query heads) at
+    batch 4 x 131072-token prefixes. N(0,1) inputs (W scaled by 0.02), median of 30 calls with
+    events on the current stream."""
+    dev = torch.device("cuda")
+    g = torch.Generator(device=dev)
+    g.manual_seed(8)
+
+    def median_us(fn, n=30, warm=5):
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        ev[0].record()
+        for k in range(n):
+            fn()
+            ev[k + 1].record()
+        torch.cuda.synchronize()
+        t = sorted(ev[k].elapsed_time(ev[k + 1]) for k in range(n))
+        return t[n // 2] * 1e3
+
+    rows = []
+    H, V = 2688, 131072 // 8
+    w = (torch.randn(V, H, device=dev, generator=g) * 0.02).to(torch.bfloat16)
+    for M in (16, 64, 128, 512):
+        hid = torch.randn(M, H, device=dev, generator=g).to(torch.bfloat16)
+        out = torch.empty(M, V, device=dev)
+        us = median_us(lambda: bmd.tt_lmhead_logits(hid, w, out))
+        byts = 2.0 * V * H + 2.0 * M * H + 4.0 * M * V
+        rows.append({"call": "tt_lmhead_logits", "M": M, "H": H, "V": V, "us": round(us, 2),
+                     "GB_s": round(byts / us / 1e3, 1), "TFLOP_s": round(2.0 * M * H * V / us / 1e6, 1)})
+    del w, hid, out
+    B, S, Hq, Hkv, D, P = 4, 16, 16, 1, 128, 131072
+    q, kb, vb = (torch.randn(*sh, device=dev, generator=g).to(torch.bfloat16)
+                 for sh in ((B, S, Hq, D), (B, S, Hkv, D), (B, S, Hkv, D)))
+    kc = torch.randn(Hkv, B * P, D, device=dev, generator=g).to(torch.bfloat16)
+    vc = torch.randn(Hkv, B * P, D, device=dev, generator=g).to(torch.bfloat16)
+    cs = torch.arange(B, dtype=torch.int32, device=dev) * P
+    cl = torch.full((B,), P, dtype=torch.int32, device=dev)
+    ws = torch.empty(bmd.workspace_bytes("tt_block_attn", B=B, S=S, Hq=Hq, Hkv=Hkv, D=D, ctx_rows=B * P,
+                                         max_prefix=P), dtype=torch.uint8, device=dev)
+    o = torch.empty_like(q)
+    us = median_us(lambda: bmd.tt_block_attn(q, kb, vb, kc, vc, cs, cl, max_prefix=P, out=o, workspace=ws))
+    byts = 2.0 * (2 * Hkv * B * P * D + 2 * B * S * Hq * D + 2 * B * S * Hkv * D)
+    rows.append({"call": "tt_block_attn", "B": B, "prefix": P, "Hq": Hq, "Hkv": Hkv, "D": D, "us": round(us, 2),
+                 "GB_s": round(byts / us / 1e3, 1)})
+    return {"metric": "kernels at one GPU's share of an 8-way split", "n_gpus": 1, "data": "synthetic",
+            "dtype": "bf16", "share": rows}
 
 
 def algorithmic(wl):
@@ -146,6 +200,9 @@ def main():
     import block_mask_diffusion_amd as bmd
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.share:
+        print(json.dumps(share(torch, bmd)))
+        return
     wl = synth.workload(args.workload)
     dev = torch.device("cuda")
 
