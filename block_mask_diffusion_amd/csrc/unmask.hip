@@ -177,7 +177,9 @@ __global__ __launch_bounds__(CM_THREADS) void unmask_commit(const Partial* __res
   const bool masked = (i < S) && ((bits >> i) & 1ull);
   float m = -INFINITY, s = 0.f;
   int a = INT32_MAX;
-  if (masked) {
+  // Every row of the block loads its records without waiting for the mask word (a row that is not
+  // masked holds stale records, in bounds, that are dropped below): one memory round trip less.
+  if (i < S) {
     const Partial* p = ws + (size_t)(b * S + i) * nchunk;
     for (int c0 = q; c0 < nchunk; c0 += CM_Q * CM_BATCH) {
       Partial x[CM_BATCH];
@@ -190,6 +192,11 @@ __global__ __launch_bounds__(CM_THREADS) void unmask_commit(const Partial* __res
 #pragma unroll
       for (int k = 0; k < CM_BATCH; ++k) merge(m, a, s, x[k].m, x[k].a, x[k].s, cs);
     }
+  }
+  if (!masked) {
+    m = -INFINITY;
+    s = 0.f;
+    a = INT32_MAX;
   }
   pm[q][i] = m;
   ps[q][i] = s;
@@ -220,8 +227,8 @@ __global__ __launch_bounds__(CM_THREADS) void unmask_commit(const Partial* __res
     }
     if (__popcll(sel) < k) {
       int rank = 0;  // place among the masked positions: higher conf first, then lower position
-      for (int j = 0; j < S; ++j) {
-        float cj = __shfl(conf, j, TT_WAVE);
+      for (int j = 0; j < S; ++j) {  // j is uniform: a scalar read of lane j
+        const float cj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(conf), j));
         bool mj = (mk >> j) & 1ull;
         rank += (mj && (cj > conf || (cj == conf && j < i))) ? 1 : 0;
       }
