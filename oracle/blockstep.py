@@ -144,24 +144,38 @@ def context_extend(inp: dict, dtype: str, rows: Optional[Iterable[Tuple[int, int
     starts = np.asarray(inp["ctx_start"], dtype=np.int64)
     lens = np.asarray(inp["ctx_len"], dtype=np.int64)
 
-    def attend_one(b: int, s: int, h: int) -> np.ndarray:
-        g = h // G
-        a, n = int(starts[b]), int(lens[b])
-        K = np.concatenate([decode(inp["k_ctx"][g, a:a + n], dtype),
-                            decode(inp["k_blk"][b, :s + 1, g], dtype)], axis=0)
-        Vv = np.concatenate([decode(inp["v_ctx"][g, a:a + n], dtype),
-                             decode(inp["v_blk"][b, :s + 1, g], dtype)], axis=0)
-        z = scale * (K @ decode(q[b, s, h], dtype))
-        e = np.exp(z - z.max())
-        return (e / e.sum()) @ Vv
+    def attend(kpre: np.ndarray, vpre: np.ndarray, b: int, g: int, s: int, heads: Sequence[int]) -> np.ndarray:
+        """Outputs of query heads `heads` (all in kv group g) at position s of sequence b, given
+        that sequence's decoded prefix rows kpre / vpre of kv head g: each row is
+        softmax(scale * K q) V over the prefix and new rows 0..s (the heads of one position see
+        the same keys, so their score rows are one product)."""
+        K = np.concatenate([kpre, decode(inp["k_blk"][b, :s + 1, g], dtype)], axis=0)
+        Vv = np.concatenate([vpre, decode(inp["v_blk"][b, :s + 1, g], dtype)], axis=0)
+        z = scale * (decode(q[b, s, heads], dtype) @ K.T)   # [heads][keys]
+        e = np.exp(z - z.max(axis=1, keepdims=True))
+        return (e / e.sum(axis=1, keepdims=True)) @ Vv
 
+    want = {}
     if rows is not None:
-        return {(int(b), int(s), int(h)): attend_one(int(b), int(s), int(h)) for (b, s, h) in rows}
+        for (b, s, h) in rows:
+            want.setdefault((int(b), int(h) // G), {}).setdefault(int(s), []).append(int(h))
+    else:
+        for b in range(B):
+            for g in range(Hkv):
+                want[(b, g)] = {s: list(range(g * G, (g + 1) * G)) for s in range(S)}
+    got = {}
+    for (b, g), by_s in want.items():
+        a, n = int(starts[b]), int(lens[b])
+        kpre = decode(inp["k_ctx"][g, a:a + n], dtype)
+        vpre = decode(inp["v_ctx"][g, a:a + n], dtype)
+        for s, heads in by_s.items():
+            for h, o in zip(heads, attend(kpre, vpre, b, g, s, heads)):
+                got[(b, s, h)] = o
+    if rows is not None:
+        return {(int(b), int(s), int(h)): got[(int(b), int(s), int(h))] for (b, s, h) in rows}
     out = np.zeros((B, S, Hq, D), dtype=np.float64)
-    for b in range(B):
-        for s in range(S):
-            for h in range(Hq):
-                out[b, s, h] = attend_one(b, s, h)
+    for (b, s, h), o in got.items():
+        out[b, s, h] = o
     k_ctx = np.array(inp["k_ctx"], copy=True)
     v_ctx = np.array(inp["v_ctx"], copy=True)
     for b in range(B):
