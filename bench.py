@@ -8,10 +8,14 @@ and confidence unmasking. Steps cycle through the T = 16 steps of a block; at ea
 boundary the block state (tokens, mask bits) is reset from a pristine copy. Inputs are seeded
 synthetic tensors (synth), uploaded to HBM before the timed region.
 
-Prints one JSON line. `value` = denoise block-steps per second (a block-step = one step of one
-block that still had a masked position at the start of the step); committed tokens/s and
-per-kernel rooflines ride along. Per-kernel durations come from HIP events recorded on the
-stream the kernels are launched on, around every call inside the timed region.
+The default workload is the largest one that fits one GPU: batch 4, 131072-token prefixes, six
+attention layers with separate caches (attention is most of its step).
+
+Prints one JSON line. `value` = denoise block-steps per second over the K timed steps (a
+block-step = one step of one block that still had a masked position at the start of the step);
+committed tokens/s and per-kernel rooflines ride along. The timed step loop carries no per-call
+events; per-call durations are medians over their own loop afterwards (each launch between two
+HIP events on the stream the kernels are launched on).
 """
 from __future__ import annotations
 
@@ -29,6 +33,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "denoise block-steps/s + committed tokens/s; % HBM roofline (attn), % MFMA (LM head)"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+ATTN_KERNELS = "attn_partial + attn_combine"
 MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 MFMA
 
 
@@ -37,11 +42,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=64)
     ap.add_argument("--warmup", type=int, default=16)
-    ap.add_argument("--workload", type=int, default=1, choices=[1, 2, 3, 4])
+    ap.add_argument("--workload", type=int, default=4, choices=[1, 2, 3, 4],
+                    help="1-4: the batch-1 2K, batch-8 8K, ragged batch-32 and batch-4 128K six-layer workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--event-stride", type=int, default=8,
-                    help="per-call timing events on every N-th timed step only (each event is a queue "
-                         "marker that adds a few microseconds of GPU time to its step)")
     ap.add_argument("--cpu-steps", type=int, default=2, help="oracle block-steps in the CPU sample")
     ap.add_argument("--copy-calib", action="store_true",
                     help="run a 1 GiB device copy first (calibrates HBM byte counters)")
@@ -116,8 +119,9 @@ def algorithmic(wl):
     return dict(attn_bytes=attn_bytes, attn_flops=attn_flops, lm_bytes=lm_bytes, lm_flops=lm_flops)
 
 
-TRAFFIC_SOURCES = {"lmhead": ("lmhead.hip", "lmhead_int.h", "reduce_int.h", "common.h"),
-                   "attn": ("attn.hip", "common.h")}
+TRAFFIC_SOURCES = {"lmhead": ("lmhead.hip", "gemm.hip", "lmhead_int.h", "reduce_int.h", "common.h"),
+                   "attn": ("attn.hip", "common.h"),
+                   "unmask": ("unmask.hip", "lmhead_int.h", "reduce_int.h", "common.h")}
 
 
 def read_traffic(kind, wid):
@@ -189,6 +193,40 @@ def cpu_baseline(wl, host, steps):
             "seconds": dt}
 
 
+def lmhead_kernel_name(M, H, V, dtype="bf16"):
+    """The kernel tt_lmhead_logits launches for these sizes: the library's own choice (lmhead.hip,
+    lm_use_lds / lm_bf16; gemm.hip, gemm_wm) written out, for the roofline's label."""
+    if dtype != "bf16":
+        return "lmhead_kernel"
+    if H % 64 == 0 and (M <= 16 or (M <= 128 and (V + 511) // 512 <= 64 and V * M <= 1 << 21)):
+        return "lmhead_lds_kernel"
+    if M > 16 and H % 64 == 0:
+        wm = 1 if (M <= 128 and (V + 511) // 512 > 64) else 2
+        return f"lmhead_gemm_kernel<{wm}>"
+    return "lmhead_kernel"
+
+
+def median_us(torch, stream, fn, n, warm=5, before=None):
+    """Median duration of fn() over n launches after `warm` untimed ones, each bracketed by its own
+    pair of HIP events on `stream` (the stream the library launches on). before(i), if given, runs
+    ahead of launch i outside its events (state resets)."""
+    for i in range(warm):
+        if before:
+            before(i)
+        fn(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i in range(n):
+        if before:
+            before(i)
+        ev[i][0].record(stream)
+        fn(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+    return t[n // 2] if n % 2 else 0.5 * (t[n // 2 - 1] + t[n // 2])
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -232,21 +270,26 @@ def main():
                     tokens=st0["tokens"], bits=st0["mask_bits"])
     del lm
     gen_s = time.perf_counter() - t_gen
+    print(f"bench: workload w{wl.wid} ({wl.name}) inputs ready in {gen_s:.1f} s", file=sys.stderr, flush=True)
 
     # synthetic spikes: one entry per logits row, added with a single scatter_add_ on the flat view
     spk_idx_d = torch.from_numpy(np.arange(wl.M, dtype=np.int64) * wl.V + sp["tok"]).to(dev)
     spk_val_d = torch.from_numpy(sp["val"]).to(dev)
+    spk_tok_d = torch.from_numpy(sp["tok"].astype(np.int32)).to(dev)
     tok0_d, bits0_d = up(st0["tokens"]), up(st0["mask_bits"])
     tokens_d, bits_d = tok0_d.clone(), bits0_d.clone()
     logits_d = torch.empty((wl.M, wl.V), dtype=torch.float32, device=dev)
     attn_out = [torch.empty_like(a["q"]) for a in attn_d]
     K, Wm = args.steps, args.warmup
     nm_hist = torch.zeros((K, wl.B), dtype=torch.int32, device=dev)
+    nm_hist_fu = torch.zeros((K, wl.B), dtype=torch.int32, device=dev)
     nm_scratch = torch.zeros((wl.B,), dtype=torch.int32, device=dev)
     ws_attn = torch.empty(bmd.workspace_bytes("tt_block_attn", B=wl.B, S=wl.S, Hq=wl.Hq, Hkv=wl.Hkv, D=wl.D,
                                               ctx_rows=wl.ctx_rows, max_prefix=wl.max_prefix),
                           dtype=torch.uint8, device=dev)
     ws_um = torch.empty(max(256, bmd.workspace_bytes("tt_confidence_unmask", B=wl.B, S=wl.S, V=wl.V)),
+                        dtype=torch.uint8, device=dev)
+    ws_fu = torch.empty(max(256, bmd.workspace_bytes("tt_lmhead_unmask", B=wl.B, S=wl.S, H=wl.H, V=wl.V)),
                         dtype=torch.uint8, device=dev)
 
     if args.copy_calib:
@@ -258,87 +301,76 @@ def main():
 
     stream = torch.cuda.current_stream()
 
-    def step(t, nm_out, ev=None):
-        s = t % wl.T
-        if s == 0:
-            tokens_d.copy_(tok0_d)
-            bits_d.copy_(bits0_d)
-        if ev is not None:
-            ev[0].record(stream)
-        for a, o in zip(attn_d, attn_out):
-            bmd.tt_block_attn(a["q"], a["k_blk"], a["v_blk"], a["k_ctx"], a["v_ctx"], a["ctx_start"],
-                              a["ctx_len"], max_prefix=wl.max_prefix, softmax_scale=a["scale"], out=o,
-                              workspace=ws_attn)
-        if ev is not None:
-            ev[1].record(stream)
+    def attn(layer):
+        a = attn_d[layer]
+        bmd.tt_block_attn(a["q"], a["k_blk"], a["v_blk"], a["k_ctx"], a["v_ctx"], a["ctx_start"], a["ctx_len"],
+                          max_prefix=wl.max_prefix, softmax_scale=a["scale"], out=attn_out[layer], workspace=ws_attn)
+
+    def lmhead():
         bmd.tt_lmhead_logits(hidden_d, w_d, logits_d)
-        if ev is not None:
-            ev[2].record(stream)
+
+    def spikes():
         logits_d.view(-1).scatter_add_(0, spk_idx_d, spk_val_d)  # synthetic spikes (one per row)
-        if ev is not None:
-            ev[3].record(stream)
+
+    def unmask(s, nm_out):
         bmd.tt_confidence_unmask(logits_d, tokens_d, bits_d, nm_out, s, wl.T, wl.gamma, wl.mask_id,
                                  workspace=ws_um)
-        if ev is not None:
-            ev[4].record(stream)
+
+    def fused(s, nm_out):
+        bmd.tt_lmhead_unmask(hidden_d, w_d, tokens_d, bits_d, nm_out, s, wl.T, wl.gamma, wl.mask_id,
+                             bias_tok=spk_tok_d, bias_val=spk_val_d, workspace=ws_fu)
+
+    def reset():
+        tokens_d.copy_(tok0_d)
+        bits_d.copy_(bits0_d)
+
+    def step(t, nm_out):
+        s = t % wl.T
+        if s == 0:
+            reset()
+        for layer in range(wl.layers):
+            attn(layer)
+        lmhead()
+        spikes()
+        unmask(s, nm_out)
 
     # the fused leg: the same step with tt_lmhead_unmask in place of LM head + spikes + unmask
     # (the spikes enter as its one-entry-per-row logit bias; the logits are never stored)
-    spk_tok_d = torch.from_numpy(sp["tok"].astype(np.int32)).to(dev)
-    ws_fu = torch.empty(max(256, bmd.workspace_bytes("tt_lmhead_unmask", B=wl.B, S=wl.S, H=wl.H, V=wl.V)),
-                        dtype=torch.uint8, device=dev)
-    nm_hist_fu = torch.zeros((K, wl.B), dtype=torch.int32, device=dev)
-
-    def step_fused(t, nm_out, ev=None):
+    def step_fused(t, nm_out):
         s = t % wl.T
         if s == 0:
-            tokens_d.copy_(tok0_d)
-            bits_d.copy_(bits0_d)
-        if ev is not None:
-            ev[0].record(stream)
-        for a, o in zip(attn_d, attn_out):
-            bmd.tt_block_attn(a["q"], a["k_blk"], a["v_blk"], a["k_ctx"], a["v_ctx"], a["ctx_start"],
-                              a["ctx_len"], max_prefix=wl.max_prefix, softmax_scale=a["scale"], out=o,
-                              workspace=ws_attn)
-        if ev is not None:
-            ev[1].record(stream)
-        bmd.tt_lmhead_unmask(hidden_d, w_d, tokens_d, bits_d, nm_out, s, wl.T, wl.gamma, wl.mask_id,
-                             bias_tok=spk_tok_d, bias_val=spk_val_d, workspace=ws_fu)
-        if ev is not None:
-            ev[2].record(stream)
+            reset()
+        for layer in range(wl.layers):
+            attn(layer)
+        fused(s, nm_out)
 
-    for t in range(Wm):
-        step(t, nm_scratch)
-    torch.cuda.synchronize()
+    def timed_loop(fn, hist):
+        for t in range(Wm):
+            fn(t, nm_scratch)
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t_wall = time.perf_counter()
+        start.record(stream)
+        for t in range(K):
+            fn(t, hist[t])
+        end.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end), time.perf_counter() - t_wall
 
-    # per-call events on every stride-th timed step (the sampled steps); the others run bare
-    stride = max(1, args.event_stride)
-    n_ev = (K + stride - 1) // stride
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(n_ev)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter()
-    start.record(stream)
-    for t in range(K):
-        step(t, nm_hist[t], evs[t // stride] if t % stride == 0 else None)
-    end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_wall
-    total_ms = start.elapsed_time(end)
+    total_ms, wall = timed_loop(step, nm_hist)
+    total_ms_fu, _ = timed_loop(step_fused, nm_hist_fu)
+    print(f"bench: timed loops done ({total_ms / K:.3f} ms/step three-call, {total_ms_fu / K:.3f} fused)",
+          file=sys.stderr, flush=True)
 
-    # fused leg, timed the same way after its own warmup
-    for t in range(Wm):
-        step_fused(t, nm_scratch)
-    evs_fu = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_ev)]
-    start_fu, end_fu = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start_fu.record(stream)
-    for t in range(K):
-        step_fused(t, nm_hist_fu[t], evs_fu[t // stride] if t % stride == 0 else None)
-    end_fu.record(stream)
-    torch.cuda.synchronize()
-    total_ms_fu = start_fu.elapsed_time(end_fu)
-    t_fu = sum(e[1].elapsed_time(e[2]) for e in evs_fu) / n_ev
+    # per-call medians, each call launched alone between two events: attention cycles through the
+    # layers (each layer's cache is cold again by its next turn at the six-layer workload); the
+    # unmask calls start from the step-0 state (every masked row read), reset outside the events
+    NC = max(20, K)
+    t_attn = median_us(torch, stream, lambda i: attn(i % wl.layers), NC)
+    t_lm = median_us(torch, stream, lambda i: lmhead(), NC)
+    t_spk = median_us(torch, stream, lambda i: spikes(), NC)
+    t_um = median_us(torch, stream, lambda i: unmask(0, nm_scratch), NC, before=lambda i: reset())
+    t_fu = median_us(torch, stream, lambda i: fused(0, nm_scratch), NC, before=lambda i: reset())
 
     # the context tower's step over a committed block (once per block in the outer loop, not part
     # of the denoiser step): one layer's tt_context_extend on layer 0's cache, laid out again with
@@ -358,83 +390,67 @@ def main():
     ext_out = torch.empty_like(a0["q"])
     ws_ext = torch.empty(bmd.workspace_bytes("tt_block_attn", B=wl.B, S=wl.S, Hq=wl.Hq, Hkv=wl.Hkv, D=wl.D,
                                              ctx_rows=R2, max_prefix=wl.max_prefix), dtype=torch.uint8, device=dev)
-    t_ext = []
-    for i in range(4 + 8):
-        ext_len.copy_(len0)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
+
+    def ext(i):
         bmd.tt_context_extend(a0["q"], a0["k_blk"], a0["v_blk"], kc2, vc2, ext_start, ext_len,
                               max_prefix=wl.max_prefix, softmax_scale=a0["scale"], out=ext_out, workspace=ws_ext)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        if i >= 4:
-            t_ext.append(e0.elapsed_time(e1))
-    t_ext = sum(t_ext) / len(t_ext)
-    del kc2, vc2
 
-    t_attn = sum(e[0].elapsed_time(e[1]) for e in evs) / n_ev
-    t_lm = sum(e[1].elapsed_time(e[2]) for e in evs) / n_ev
-    t_spk = sum(e[2].elapsed_time(e[3]) for e in evs) / n_ev
-    t_um = sum(e[3].elapsed_time(e[4]) for e in evs) / n_ev
+    t_ext = median_us(torch, stream, ext, NC, before=lambda i: ext_len.copy_(len0))
+    del kc2, vc2
 
     # block-steps and commits from the per-step n_masked record
     init_masked = np.array([bin(int(b)).count("1") for b in st0["mask_bits"]])
 
     def tally(nm):
-        # masked rows are counted on the steps that carried timing events, whose unmask time
-        # they go with (the unmask reads the still-masked rows only)
-        block_steps, commits, masked_rows = 0, 0, 0
+        block_steps, commits = 0, 0
         for t in range(K):
             start_masked = init_masked if t % wl.T == 0 else nm[t - 1]
             block_steps += int(np.sum(start_masked > 0))
             commits += int(np.sum(start_masked - nm[t]))
-            if t % stride == 0:
-                masked_rows += int(np.sum(start_masked))
-        return block_steps, commits, masked_rows
+        return block_steps, commits
 
-    block_steps, commits, masked_rows = tally(nm_hist.cpu().numpy())
-    block_steps_fu, commits_fu, _ = tally(nm_hist_fu.cpu().numpy())
-    sec = total_ms / 1e3
-    sec_fu = total_ms_fu / 1e3
+    block_steps, commits = tally(nm_hist.cpu().numpy())
+    block_steps_fu, commits_fu = tally(nm_hist_fu.cpu().numpy())
+    sec, sec_fu = total_ms / 1e3, total_ms_fu / 1e3
     alg = algorithmic(wl)
-    lm_gbs = alg["lm_bytes"] / (t_lm / 1e3) / 1e9
+    lm_gbs = alg["lm_bytes"] / (t_lm * 1e-6) / 1e9
+    lm_tfs = alg["lm_flops"] / (t_lm * 1e-6) / 1e12
     # context extend: the attention's bytes plus the appended rows written
     ext_bytes = alg["attn_bytes"] + (2 if wl.dtype == "bf16" else 4) * 2.0 * wl.B * wl.S * wl.Hkv * wl.D
-    t_attn_call = t_attn / wl.layers  # ms per tt_block_attn call (one layer)
-    attn_gbs = alg["attn_bytes"] / (t_attn_call / 1e3) / 1e9
-    um_bytes = 4.0 * wl.V * masked_rows / n_ev
-    um_gbs = um_bytes / (t_um / 1e3) / 1e9
-    lm_tfs = alg["lm_flops"] / (t_lm / 1e3) / 1e12
-    attn_tfs = alg["attn_flops"] / (t_attn_call / 1e3) / 1e12
+    attn_gbs = alg["attn_bytes"] / (t_attn * 1e-6) / 1e9
+    attn_tfs = alg["attn_flops"] / (t_attn * 1e-6) / 1e12
+    um_bytes = 4.0 * wl.V * int(init_masked.sum())
+    um_gbs = um_bytes / (t_um * 1e-6) / 1e9
     # attainable LM-head rate: min(MFMA peak, arithmetic intensity x HBM peak)
     lm_attain_tfs = min(MFMA_BF16_PEAK_TFS, alg["lm_flops"] / alg["lm_bytes"] * HBM_PEAK_GBS / 1e3)
 
-    times = {"attn": t_attn, "lmhead": t_lm, "unmask": t_um}
-    dominant = max(times, key=times.get)
+    per_step = {"attn": t_attn * wl.layers, "lmhead": t_lm, "unmask": t_um}
+    dominant = max(per_step, key=per_step.get)
     if dominant == "lmhead":
         traffic = read_traffic("lmhead", wl.wid)
-        lm_kernel = "lmhead_lds_kernel" if wl.M <= 64 else "lmhead_gemm_kernel"
+        lm_kernel = lmhead_kernel_name(wl.M, wl.H, wl.V, wl.dtype)
         ridge = MFMA_BF16_PEAK_TFS * 1e3 / HBM_PEAK_GBS  # flop per byte where the two roofs meet
         if alg["lm_flops"] / alg["lm_bytes"] >= ridge:
             roof = {"kernel": f"{lm_kernel} (tt_lmhead_logits)", "bound": "mfma", "achieved": round(lm_tfs, 1),
                     "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s", "frac": round(lm_tfs / MFMA_BF16_PEAK_TFS, 4),
-                    "traffic": traffic, "algorithmic_flops": alg["lm_flops"], "avg_launch_us": round(t_lm * 1e3, 2)}
+                    "traffic": traffic, "algorithmic_flops": alg["lm_flops"], "avg_launch_us": round(t_lm, 2)}
         else:
             roof = {"kernel": f"{lm_kernel} (tt_lmhead_logits)", "bound": "hbm", "achieved": round(lm_gbs, 1),
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(lm_gbs / HBM_PEAK_GBS, 4),
-                    "traffic": traffic, "algorithmic_bytes": alg["lm_bytes"], "avg_launch_us": round(t_lm * 1e3, 2)}
+                    "traffic": traffic, "algorithmic_bytes": alg["lm_bytes"], "avg_launch_us": round(t_lm, 2)}
     elif dominant == "attn":
-        roof = {"kernel": "attn_partial + attn_combine (tt_block_attn)", "bound": "hbm",
+        roof = {"kernel": f"{ATTN_KERNELS} (tt_block_attn, one layer)", "bound": "hbm",
                 "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": read_traffic("attn", wl.wid),
-                "algorithmic_bytes": alg["attn_bytes"], "avg_launch_us": round(t_attn_call * 1e3, 2)}
+                "algorithmic_bytes": alg["attn_bytes"], "avg_launch_us": round(t_attn, 2)}
     else:
         roof = {"kernel": "unmask (tt_confidence_unmask)", "bound": "hbm", "achieved": round(um_gbs, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(um_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                "algorithmic_bytes": um_bytes, "avg_launch_us": round(t_um * 1e3, 2)}
+                "algorithmic_bytes": um_bytes, "avg_launch_us": round(t_um, 2)}
 
     cpu = None
     if want_cpu:
+        print("bench: CPU baseline (the oracle) ...", file=sys.stderr, flush=True)
         cpu = cpu_baseline(wl, host, args.cpu_steps)
         cpu.pop("seconds", None)
 
@@ -459,14 +475,16 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels": {
-            "attn": {"us_per_layer": round(t_attn / wl.layers * 1e3, 2), "GB_s": round(attn_gbs, 1),
+            "attn": {"us_per_layer": round(t_attn, 2), "GB_s": round(attn_gbs, 1),
                      "hbm_frac": round(attn_gbs / HBM_PEAK_GBS, 4), "TFLOP_s": round(attn_tfs, 1),
                      "mfma_frac": round(attn_tfs / MFMA_BF16_PEAK_TFS, 4)},
-            "lmhead": {"us": round(t_lm * 1e3, 2), "GB_s": round(lm_gbs, 1), "hbm_frac": round(lm_gbs / HBM_PEAK_GBS, 4),
+            "lmhead": {"kernel": lmhead_kernel_name(wl.M, wl.H, wl.V, wl.dtype), "us": round(t_lm, 2),
+                       "GB_s": round(lm_gbs, 1), "hbm_frac": round(lm_gbs / HBM_PEAK_GBS, 4),
                        "TFLOP_s": round(lm_tfs, 2), "mfma_frac": round(lm_tfs / MFMA_BF16_PEAK_TFS, 4),
                        "attainable_frac": round(lm_tfs / lm_attain_tfs, 4)},
-            "unmask": {"us": round(t_um * 1e3, 2), "GB_s": round(um_gbs, 1), "hbm_frac": round(um_gbs / HBM_PEAK_GBS, 4)},
-            "spikes_us": round(t_spk * 1e3, 2),
+            "unmask": {"us_step0": round(t_um, 2), "masked_rows_step0": int(init_masked.sum()),
+                       "GB_s": round(um_gbs, 1), "hbm_frac": round(um_gbs / HBM_PEAK_GBS, 4)},
+            "spikes_us": round(t_spk, 2),
         },
         "fused_path": {
             "what": "same step with tt_lmhead_unmask (LM head with the vocabulary reduction in its epilogue, "
@@ -474,20 +492,21 @@ def main():
             "block_steps_per_s": round(block_steps_fu / sec_fu, 2),
             "committed_tokens_per_s": round(commits_fu / sec_fu, 2),
             "ms_per_step": round(total_ms_fu / K, 4),
-            "lmhead_unmask_us": round(t_fu * 1e3, 2),
-            "lmhead_unmask_hbm_frac": round((alg["lm_bytes"] - 4.0 * wl.M * wl.V) / (t_fu / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
-            "lmhead_unmask_mfma_frac": round(alg["lm_flops"] / (t_fu / 1e3) / 1e12 / MFMA_BF16_PEAK_TFS, 4),
+            "lmhead_unmask_us_step0": round(t_fu, 2),
+            "lmhead_unmask_hbm_frac": round((alg["lm_bytes"] - 4.0 * wl.M * wl.V) / (t_fu * 1e-6) / 1e9
+                                            / HBM_PEAK_GBS, 4),
+            "lmhead_unmask_mfma_frac": round(alg["lm_flops"] / (t_fu * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFS, 4),
         },
         "context_extend": {
             "what": "tt_context_extend, one layer: causal attention of the S committed tokens over "
                     "[cache ; block], then the append of their K/V (once per block, not in the step)",
-            "us": round(t_ext * 1e3, 2),
-            "GB_s": round(ext_bytes / (t_ext / 1e3) / 1e9, 1),
-            "hbm_frac": round(ext_bytes / (t_ext / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+            "us": round(t_ext, 2),
+            "GB_s": round(ext_bytes / (t_ext * 1e-6) / 1e9, 1),
+            "hbm_frac": round(ext_bytes / (t_ext * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
         },
-        "timing": {"per_call_events_every": stride, "steps_with_events": n_ev,
-                   "note": "per-call times (kernels, roofline) average the steps with events; "
-                           "value and ms_per_step cover all timed steps"},
+        "timing": {"per_call": f"median of {NC} launches after 5 warm-ups, each between two HIP events on "
+                               "the launch stream, after the step loops",
+                   "step_loop": f"{K} steps between two events, no per-call events inside"},
         "wall_s_timed": round(wall, 3),
         "input_gen_s": round(gen_s, 1),
     }

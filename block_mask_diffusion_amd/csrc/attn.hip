@@ -800,7 +800,8 @@ __global__ __launch_bounds__(CB_THREADS) void attn_combine(Args<T, D> A) {
     for (int k = 0; k < CB; ++k) {
       const int wk = w0 + NSG * k;
       const size_t slot = (size_t)wk + u;
-      if (wk <= wl) {
+      // a workgroup whose key range is empty (fewer keys than workgroups) wrote no partial
+      if (wk <= wl && (int64_t)wk * Ttot / A.W < (int64_t)(wk + 1) * Ttot / A.W) {
         ml[k] = A.ws_ml[slot * R + row];
         ov[k] = *reinterpret_cast<const u32x4*>(
             A.ws_o + ((((slot * RW + row / 32) * (D / 8) + quad / 2) * 2 + quad % 2) * 32 + row % 32) * VPT);

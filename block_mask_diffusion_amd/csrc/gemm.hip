@@ -96,9 +96,12 @@ __global__ __launch_bounds__(LM_THREADS, 1) __attribute__((amdgpu_waves_per_eu(1
     if (red.mask_bits) {
       __shared__ int scan[LM_THREADS];
       int base = 0;
+      // only bits 0 .. S-1 name positions of a block; higher bits are ignored (a stray one would
+      // name a row of the next block, or one past M)
+      const uint64_t valid = red.S >= 64 ? ~0ull : ((1ull << red.S) - 1);
       for (int b0 = 0; b0 < red.B; b0 += LM_THREADS) {
         const int b = b0 + tid;
-        uint64_t bits = b < red.B ? red.mask_bits[b] : 0ull;
+        uint64_t bits = b < red.B ? (red.mask_bits[b] & valid) : 0ull;
         const int c = __popcll(bits);
         scan[tid] = c;
         __syncthreads();

@@ -149,6 +149,7 @@ int tt_lmhead_logits(const void* hidden, const void* w, float* logits,
  *   if |C| < k, C = the k most confident positions of Mk (ties: lower position first);
  *   tokens[b][i] = pred_i and bit i cleared for i in C; n_masked[b] = |Mk| - |C|.
  * Positions outside Mk are never read (their logits rows may hold anything) nor written.
+ * Bits S..63 of a mask word name no position: they are ignored and stored back unchanged.
  * Layouts: logits fp32 [B*S][V] (row b*S+i is position i of block b); tokens int32 [B][S]
  *   (in/out); mask_bits uint64 [B] (in/out; bit i = position i still masked); n_masked int32 [B]
  *   (out). conf_out fp32 [B*S] and pred_out int32 [B*S] are optional (NULL = not written); when

@@ -79,12 +79,18 @@ def _sampled_check(wl, layer=0, n=48, seed=0):
     assert float(np.abs(got).max()) <= vmax
 
 
-def test_workload_3_ragged_sampled():
-    _sampled_check(synth.workload(3))
+def test_workload_3_ragged_full():
+    """Every output row of the ragged batch-32 workload (64 units, prefixes 512 to 32768)."""
+    _full_check(synth.workload(3))
 
 
-def test_workload_4_one_layer_sampled():
-    _sampled_check(synth.workload(4), layer=5)
+def test_workload_4_one_layer_full():
+    """Every output row of one layer of the batch-4, 131072-token-prefix workload."""
+    _full_check(synth.workload(4), layer=5)
+
+
+def test_workload_4_other_layer_sampled():
+    _sampled_check(synth.workload(4), layer=2)
 
 
 def test_block_key_permutation_invariance():
@@ -210,3 +216,60 @@ def test_lengths_outside_the_contract_are_clamped():
     # the arrays themselves are inputs only
     assert np.array_equal(d["ctx_start"].cpu().numpy(), start)
     assert np.array_equal(d["ctx_len"].cpu().numpy(), length)
+
+
+def _nan_workspace(nbytes):
+    return torch.full((max(nbytes, 256),), 0xFF, dtype=torch.uint8, device="cuda")  # fp32 NaN bytes
+
+
+@pytest.mark.parametrize("B,prefixes,max_prefix", [(1, [0], 4096), (1, [100], 131072), (2, [0, 5], 8192),
+                                                   (2, [3, 0], 131072), (2, [40, 300], 65536)])
+def test_short_sequences_against_a_large_max_prefix(B, prefixes, max_prefix):
+    """max_prefix sizes the launch (its workgroup count), the lengths on the device may be far
+    shorter: most workgroups then own no keys and write no partial. The merge must read only the
+    partials that were written; a workspace filled with NaN shows any stale read."""
+    wl = _wl(1, B=B, prefixes=prefixes)
+    wl.wid = 1300 + sum(prefixes) + max_prefix % 97
+    inp = synth.attn_inputs(wl)
+    # the cache holds 64 rows more than the sequences use (never attended: a cache sized for
+    # later blocks), so it is not empty even when every length is 0
+    spare = synth._store(synth._normal(synth.rng(wl.wid, synth.T_SPARE), (wl.Hkv, 64, wl.D)), wl.dtype)
+    inp["k_ctx"] = np.concatenate([inp["k_ctx"], spare], axis=1)
+    inp["v_ctx"] = np.concatenate([inp["v_ctx"], spare[:, ::-1]], axis=1)
+    d = attn_dev(inp)
+    n = bmd.workspace_bytes("tt_block_attn", B=B, S=wl.S, Hq=wl.Hq, Hkv=wl.Hkv, D=wl.D,
+                            ctx_rows=inp["k_ctx"].shape[1], max_prefix=max_prefix)
+    out = bmd.tt_block_attn(d["q"], d["k_blk"], d["v_blk"], d["k_ctx"], d["v_ctx"], d["ctx_start"], d["ctx_len"],
+                            max_prefix=max_prefix, softmax_scale=d["scale"], workspace=_nan_workspace(n))
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    ref = oracle.block_attention(inp, wl.dtype)
+    assert np.all(np.isfinite(got))
+    assert float(np.max(np.abs(got - ref))) <= ATOL_BF16
+
+
+@pytest.mark.parametrize("B,prefixes,max_prefix", [(1, [0], 4096), (2, [0, 5], 8192), (2, [40, 300], 16384)])
+def test_context_extend_short_sequences_against_a_large_max_prefix(B, prefixes, max_prefix):
+    """The same for the context tower's step: a cache with room for max_prefix + S rows, short
+    sequences in it, a NaN-filled workspace."""
+    wl = _wl(1, B=B, prefixes=prefixes)
+    wl.wid = 1350 + sum(prefixes)
+    inp = synth.context_inputs(wl)
+    R = max_prefix + wl.S + inp["k_ctx"].shape[1]
+    pad = ((0, 0), (0, R - inp["k_ctx"].shape[1]), (0, 0))
+    inp["k_ctx"] = np.pad(inp["k_ctx"], pad)
+    inp["v_ctx"] = np.pad(inp["v_ctx"], pad)
+    d = attn_dev(inp)
+    n = bmd.workspace_bytes("tt_block_attn", B=B, S=wl.S, Hq=wl.Hq, Hkv=wl.Hkv, D=wl.D, ctx_rows=R,
+                            max_prefix=max_prefix)
+    out = bmd.tt_context_extend(d["q"], d["k_blk"], d["v_blk"], d["k_ctx"], d["v_ctx"], d["ctx_start"],
+                                d["ctx_len"], max_prefix=max_prefix, softmax_scale=d["scale"],
+                                workspace=_nan_workspace(n))
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    ref, kc, vc, ln = oracle.context_extend(inp, wl.dtype)
+    assert np.all(np.isfinite(got))
+    assert float(np.max(np.abs(got - ref))) <= ATOL_BF16
+    assert np.array_equal(d["ctx_len"].cpu().numpy(), ln)
+    assert np.array_equal(d["k_ctx"].view(torch.int16).cpu().numpy().view(np.uint16), kc)
+    assert np.array_equal(d["v_ctx"].view(torch.int16).cpu().numpy().view(np.uint16), vc)

@@ -89,17 +89,14 @@ def test_key_split_cuts_inside_the_block():
     assert found == 3
 
 
-def test_workload_shape_full_prefix_sampled():
-    """128K-token prefixes (the benchmark's largest shape, one layer): sampled rows against the
-    oracle one by one, every appended row and the lengths exactly."""
+def test_workload_shape_full_prefix():
+    """128K-token prefixes (the benchmark's largest shape, one layer): every output row against
+    the oracle, every appended row and the lengths exactly."""
     wl = synth.workload(4)
     inp = synth.context_inputs(wl)
     got, kc, vc, ln = _run(inp, wl)
-    g = np.random.default_rng(4)
-    rows = [(int(g.integers(wl.B)), int(g.integers(wl.S)), int(g.integers(wl.Hq))) for _ in range(24)]
-    rows += [(0, 0, 0), (wl.B - 1, wl.S - 1, wl.Hq - 1), (1, 0, 31), (2, 15, 0)]
-    ref = oracle.context_extend(inp, "bf16", rows=rows)
-    err = max(float(np.max(np.abs(got[b, s, h] - ref[(b, s, h)]))) for (b, s, h) in rows)
+    ref = oracle.context_extend(inp, "bf16")[0]
+    err = float(np.max(np.abs(got - ref)))
     assert err <= ATOL_BF16, err
     assert list(ln) == [p + wl.S for p in wl.prefixes]
     for b in range(wl.B):

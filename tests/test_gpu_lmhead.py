@@ -67,20 +67,17 @@ def test_one_hot_hidden_reads_weight_columns_exactly():
 
 
 @pytest.mark.parametrize("wid", [1, 2, 3, 4])
-def test_workload_full_size_sampled(wid):
+def test_workload_full_size(wid):
+    """The whole M x 131072 logits matrix of each workload (H = 2688) against the oracle: within
+    1e-2 and within the fp32 accumulation bound, entry by entry."""
     wl = synth.workload(wid)
     inp = synth.lmhead_inputs(wl)
     got = _run(inp)
-    g = np.random.default_rng(wid)
-    pairs = [(int(g.integers(wl.M)), int(g.integers(wl.V))) for _ in range(3000)]
-    pairs += [(0, 0), (wl.M - 1, wl.V - 1), (wl.M - 1, 0), (0, wl.V - 1)]
-    ref = oracle.lmhead_entries(inp["hidden"], inp["w"], "bf16", pairs)
-    gv = np.array([got[m, v] for (m, v) in pairs])
-    assert float(np.max(np.abs(gv - ref))) <= ATOL_BF16
-    # one full row against the oracle as well
-    m = wl.M // 2
-    rowref = oracle.decode(inp["w"], "bf16") @ oracle.decode(inp["hidden"][m], "bf16")
-    assert float(np.max(np.abs(got[m] - rowref))) <= ATOL_BF16
+    ref = oracle.lmhead_logits(inp["hidden"], inp["w"], "bf16")
+    err = np.abs(got - ref)
+    print(f"w{wid}: logits max abs err {float(err.max()):.3e}")
+    assert float(err.max()) <= ATOL_BF16
+    assert np.all(err <= _bound(inp, "bf16") + np.abs(ref) * 2.0 ** -24)
 
 
 def test_deterministic():

@@ -125,7 +125,8 @@ def test_fused_with_sampler(B, kind, tau):
         torch.cuda.synchronize()
         g = dict(tokens=tok_d.cpu().numpy(), mask_bits=host_bits(bits_d), n_masked=nm.cpu().numpy(),
                  conf=conf.cpu().numpy().reshape(B, wl.S), pred=pred.cpu().numpy().reshape(B, wl.S))
-        check_fused_step(wl.S, wl.gamma, step, wl.T, bits_h, g, ref, lambda m: lg[m], wl.mask_id, range(B), kind)
+        check_fused_step(wl.S, wl.gamma, step, wl.T, bits_h, g, ref, lambda m: lg[m], wl.mask_id, range(B), kind,
+                         temperature=tau)
         tokens_h, bits_h = ref["tokens"], ref["mask_bits"]
         tok_d.copy_(dev(tokens_h))
         bits_d.copy_(dev(bits_h))
