@@ -16,7 +16,8 @@ from . import _lib
 from ._lib import TTError, TT_BF16, TT_F32
 
 __all__ = ["tt_block_attn", "tt_context_extend", "tt_lmhead_logits", "tt_confidence_unmask",
-           "tt_unmask_sample", "tt_lmhead_unmask", "workspace_bytes", "TTError", "abi_version"]
+           "tt_confidence_unmask_noalloc", "tt_unmask_sample", "tt_lmhead_unmask", "workspace_bytes", "TTError",
+           "abi_version"]
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -200,6 +201,23 @@ def tt_confidence_unmask(logits: torch.Tensor, tokens: torch.Tensor, mask_bits: 
     ws = _workspace(n.value, workspace, logits.device)
     n2 = ctypes.c_size_t(ws.numel() * ws.element_size())
     _check(lib.tt_confidence_unmask(*args, _ptr(ws), ctypes.byref(n2), _stream(stream)), "tt_confidence_unmask")
+
+
+def tt_confidence_unmask_noalloc(logits: torch.Tensor, tokens: torch.Tensor, mask_bits: torch.Tensor,
+                                 n_masked: torch.Tensor, step: int, num_steps: int, gamma: float,
+                                 mask_id: int, conf_out: Optional[torch.Tensor] = None,
+                                 pred_out: Optional[torch.Tensor] = None, stream=None) -> None:
+    """tt_confidence_unmask without a workspace: the library's per-device scratch serves instead,
+    and nothing is allocated (see include/tt.h for its size limit and its sharing rule)."""
+    _need(tokens.dim() == 2 and tokens.dtype == torch.int32, "tokens int32 [B][S]")
+    B, S = tokens.shape
+    _need(logits.dtype == torch.float32 and logits.dim() == 2 and logits.shape[0] == B * S, "logits fp32 [B*S][V]")
+    V = logits.shape[1]
+    _unmask_io(B, S, tokens, mask_bits, n_masked, conf_out, pred_out)
+    _dev(logits, tokens, mask_bits, n_masked, conf_out, pred_out)
+    _check(_lib.load().tt_confidence_unmask_noalloc(
+        _ptr(logits), _ptr(tokens), _ptr(mask_bits), _ptr(n_masked), _ptr(conf_out), _ptr(pred_out), B, S, V,
+        int(step), int(num_steps), float(gamma), int(mask_id), _stream(stream)), "tt_confidence_unmask_noalloc")
 
 
 def tt_unmask_sample(logits: torch.Tensor, tokens: torch.Tensor, mask_bits: torch.Tensor,

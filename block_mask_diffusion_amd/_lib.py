@@ -22,7 +22,8 @@ TT_OK, TT_ERR_ARG, TT_ERR_UNSUPPORTED, TT_ERR_WORKSPACE, TT_ERR_HIP = 0, -1, -2,
 
 # every symbol include/tt.h declares
 EXPORTS = ("tt_block_attn", "tt_context_extend", "tt_lmhead_logits", "tt_confidence_unmask",
-           "tt_unmask_sample", "tt_lmhead_unmask", "tt_status_string", "tt_abi_version")
+           "tt_confidence_unmask_noalloc", "tt_unmask_sample", "tt_lmhead_unmask", "tt_status_string",
+           "tt_abi_version")
 
 TT_SAMPLER_CONFIDENCE, TT_SAMPLER_PREDICT_NOISE = 0, 1
 SAMPLER_KINDS = {"confidence": TT_SAMPLER_CONFIDENCE, "predict_noise": TT_SAMPLER_PREDICT_NOISE}
@@ -72,6 +73,8 @@ def load() -> ctypes.CDLL:
     lib.tt_lmhead_logits.restype = i
     lib.tt_confidence_unmask.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f32, i, vp, sz, vp]
     lib.tt_confidence_unmask.restype = i
+    lib.tt_confidence_unmask_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f32, i, vp]
+    lib.tt_confidence_unmask_noalloc.restype = i
     smp = ctypes.POINTER(Sampler)
     lib.tt_unmask_sample.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, smp, i, vp, sz, vp]
     lib.tt_unmask_sample.restype = i

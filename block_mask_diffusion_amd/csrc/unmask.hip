@@ -14,6 +14,8 @@
 // The fused LM head + unmask call (tt_lmhead_unmask) replaces the logits and unmask_partial with
 // the LM-head kernels' reduction epilogue (one record per row and column block of one wave),
 // merges each masked row's records with unmask_rowmerge and ends with the same unmask_commit.
+#include <mutex>
+
 #include "lmhead_int.h"
 #include "reduce_int.h"
 
@@ -262,26 +264,18 @@ int unmask_check(const int32_t* tokens, const uint64_t* mask_bits, const int32_t
 
 float sampler_scale(const tt_sampler* sm) { return TT_LOG2E / sm->temperature; }
 
-}  // namespace
+// Records of the unmasking step's first kernel: one per (row, vocabulary chunk).
+size_t unmask_records(int B, int S, int V) {
+  return (size_t)B * S * (size_t)((V + UM_CHUNK - 1) / UM_CHUNK);
+}
 
-extern "C" int tt_unmask_sample(const float* logits, int32_t* tokens, uint64_t* mask_bits,
-                                int32_t* n_masked, float* conf_out, int32_t* pred_out, int B, int S,
-                                int V, int step, int num_steps, const tt_sampler* sampler, int mask_id,
-                                void* workspace, size_t* workspace_bytes, void* stream) {
-  if (!logits) return TT_ERR_ARG;
-  int st = unmask_check(tokens, mask_bits, n_masked, workspace_bytes, B, S, V, step, num_steps, mask_id,
-                        sampler);
-  if (st != TT_OK) return st;
-  if (S > 64) return TT_ERR_UNSUPPORTED;
+// The two kernels of an unmasking step, with `ws` holding unmask_records(B, S, V) records
+// (arguments already checked).
+int unmask_launch(const float* logits, int32_t* tokens, uint64_t* mask_bits, int32_t* n_masked,
+                  float* conf_out, int32_t* pred_out, int B, int S, int V, int step, int num_steps,
+                  const tt_sampler* sampler, int mask_id, Partial* ws, hipStream_t s) {
   const size_t rows = (size_t)B * S;
   const int nchunk = (V + UM_CHUNK - 1) / UM_CHUNK;
-  if (rows * (size_t)nchunk > (size_t)INT32_MAX) return TT_ERR_UNSUPPORTED;
-  const size_t need = rows * nchunk * sizeof(Partial);
-  st = tt_workspace_check(workspace, workspace_bytes, need);
-  if (st != 0) return st < 0 ? st : TT_OK;
-  if ((uintptr_t)workspace % alignof(Partial)) return TT_ERR_ARG;
-  hipStream_t s = (hipStream_t)stream;
-  Partial* ws = (Partial*)workspace;
   const float cs = sampler_scale(sampler);
   const bool vec4 = (V % 4 == 0) && ((uintptr_t)logits % 16 == 0);
   dim3 grid((unsigned)(rows * nchunk));
@@ -295,6 +289,65 @@ extern "C" int tt_unmask_sample(const float* logits, int32_t* tokens, uint64_t* 
   hipLaunchKernelGGL(unmask_commit, dim3(B), dim3(CM_THREADS), 0, s, ws, tokens, mask_bits, n_masked,
                      conf_out, pred_out, S, nchunk, step, num_steps, sampler->kind, sampler->gamma, cs);
   return tt_launch_status();
+}
+
+// Scratch of tt_confidence_unmask_noalloc: the records of unmask_launch in a fixed array of each
+// device (every GPU the library runs on holds it until the process ends). Host code never uses
+// the array's name as an address: the device address is looked up once per device.
+constexpr size_t UM_SCRATCH_BYTES = (size_t)2 << 20;
+static __device__ __align__(256) unsigned char scratch[UM_SCRATCH_BYTES];
+constexpr int UM_MAX_DEVICES = 64;
+std::mutex scratch_mu;
+void* scratch_dev[UM_MAX_DEVICES];
+
+// Device address of `scratch` on the current device (nullptr if the lookup fails).
+void* scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= UM_MAX_DEVICES) return nullptr;
+  std::lock_guard<std::mutex> lk(scratch_mu);
+  if (!scratch_dev[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    scratch_dev[dev] = p;
+  }
+  return scratch_dev[dev];
+}
+
+}  // namespace
+
+extern "C" int tt_unmask_sample(const float* logits, int32_t* tokens, uint64_t* mask_bits,
+                                int32_t* n_masked, float* conf_out, int32_t* pred_out, int B, int S,
+                                int V, int step, int num_steps, const tt_sampler* sampler, int mask_id,
+                                void* workspace, size_t* workspace_bytes, void* stream) {
+  if (!logits) return TT_ERR_ARG;
+  int st = unmask_check(tokens, mask_bits, n_masked, workspace_bytes, B, S, V, step, num_steps, mask_id,
+                        sampler);
+  if (st != TT_OK) return st;
+  if (S > 64) return TT_ERR_UNSUPPORTED;
+  const size_t recs = unmask_records(B, S, V);
+  if (recs > (size_t)INT32_MAX) return TT_ERR_UNSUPPORTED;
+  st = tt_workspace_check(workspace, workspace_bytes, recs * sizeof(Partial));
+  if (st != 0) return st < 0 ? st : TT_OK;
+  if ((uintptr_t)workspace % alignof(Partial)) return TT_ERR_ARG;
+  return unmask_launch(logits, tokens, mask_bits, n_masked, conf_out, pred_out, B, S, V, step, num_steps,
+                       sampler, mask_id, (Partial*)workspace, (hipStream_t)stream);
+}
+
+extern "C" int tt_confidence_unmask_noalloc(const float* logits, int32_t* tokens, uint64_t* mask_bits,
+                                            int32_t* n_masked, float* conf_out, int32_t* pred_out, int B,
+                                            int S, int V, int step, int num_steps, float gamma, int mask_id,
+                                            void* stream) {
+  if (!logits) return TT_ERR_ARG;
+  const tt_sampler sm{TT_SAMPLER_CONFIDENCE, gamma, 1.f};
+  size_t unused = 0;
+  int st = unmask_check(tokens, mask_bits, n_masked, &unused, B, S, V, step, num_steps, mask_id, &sm);
+  if (st != TT_OK) return st;
+  if (S > 64) return TT_ERR_UNSUPPORTED;
+  if (unmask_records(B, S, V) * sizeof(Partial) > UM_SCRATCH_BYTES) return TT_ERR_WORKSPACE;
+  void* ws = scratch_ptr();
+  if (!ws) return TT_ERR_HIP;
+  return unmask_launch(logits, tokens, mask_bits, n_masked, conf_out, pred_out, B, S, V, step, num_steps, &sm,
+                       mask_id, (Partial*)ws, (hipStream_t)stream);
 }
 
 extern "C" int tt_confidence_unmask(const float* logits, int32_t* tokens, uint64_t* mask_bits,

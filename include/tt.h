@@ -167,6 +167,25 @@ int tt_confidence_unmask(const float* logits, int32_t* tokens, uint64_t* mask_bi
                          void* workspace, size_t* workspace_bytes, void* stream);
 
 /*
+ * tt_confidence_unmask_noalloc — tt_confidence_unmask for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ *
+ * Same arguments, results and errors as tt_confidence_unmask without the workspace: the call
+ * keeps its per-row, per-vocabulary-chunk records in a scratch array of 2 MiB that the library
+ * holds on each device it runs on (until the process ends), and calls no allocator.
+ * Limit: B * S * ceil(V / 4096) * 16 bytes <= 2 MiB (B * S <= 4096 at V = 131072); beyond it the
+ * call returns TT_ERR_WORKSPACE and launches nothing. TT_ERR_HIP also when the scratch's device
+ * address cannot be looked up. Nothing in the scratch needs to start at zero.
+ * Every call on one GPU shares that GPU's scratch, which keeps the last call's contents: calls
+ * that overlap in time on one GPU (other streams, other host threads) race, and the caller must
+ * serialise them.
+ */
+int tt_confidence_unmask_noalloc(const float* logits, int32_t* tokens, uint64_t* mask_bits,
+                                 int32_t* n_masked, float* conf_out, int32_t* pred_out,
+                                 int B, int S, int V, int step, int num_steps, float gamma,
+                                 int mask_id, void* stream);
+
+/*
  * tt_lmhead_unmask — tt_lmhead_logits followed by tt_confidence_unmask in one call, with the
  * vocabulary reduction done in the LM-head kernel's epilogue, so the [B*S][V] logits are never
  * stored ("Nemotron-Labs-TwoTower" wiki page, section "Block-wise generation": the step needs,
