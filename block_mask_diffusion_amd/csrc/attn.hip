@@ -39,6 +39,8 @@ constexpr int AT_MAX_B = 1024;  // sequences handled by the in-workgroup prefix 
 constexpr float LOG2E = 1.4426950408889634f;
 static_assert(MAX_ROWS == QT * AT_WAVES, "8 query tiles per workgroup");
 constexpr float RESCALE_LOG2 = 8.f;  // lazy-rescale threshold (log2 units)
+// speculative probabilities (bf16 path): a lane's sum of its 16 above this takes the slow path
+constexpr float RESCALE_SUM = 256.f;
 // K/V stage loads: every key row is read exactly once, so they stream with the non-temporal
 // policy
 #ifndef TT_AT_DMA
@@ -197,7 +199,8 @@ struct Args {
   // then writes 1 KiB and each wave 32 contiguous KiB, spread over all memory channels; the
   // combine's read of one 4-element quad of consecutive rows is contiguous as well.
   PartT<T>* ws_o;
-  float2* ws_ml;   // [slots][R]: (running max of the raw scores m, sum l relative to m)
+  float2* ws_ml;   // [slots][R]: (reference r of the partial in log2 units, i.e. a score times c;
+                   // sum l of exp2(score c - r)); r = -inf for a partial with no visible key
   int B, S, Hq, Hkv;
   int64_t ctx_rows;
   int max_prefix;
@@ -552,6 +555,7 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_partial(Args<T, D> A) {
     };
 
     f32x16 sa, sb;
+    float mc_final = 0.f;  // bf16 path: the reference its partial is relative to (log2 units)
     if constexpr (PIPE) {
       // Stage loads of the bf16 path with compile-time ring slot BUF: fast stages from the
       // piece's context rows through one scalar base per stage, others through issue_chunk.
@@ -604,20 +608,65 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_partial(Args<T, D> A) {
       };
 
       // Software pipeline over the piece's 32-key sub-tiles. Step j holds the scores of sub-tile
-      // j (sc) and the pending PV product of sub-tile j - 1; it
-      //   reads the K fragments of sub-tile j + 1 (after the barrier that makes its stage
-      //   resident), issues the PV MFMAs of sub-tile j - 1 with the row max of sub-tile j between
-      //   them, rescales (rarely), then issues the score MFMAs of sub-tile j + 1 (into sn) with
-      //   the exponentials and the V^T reads of sub-tile j between them.
+      // j (sc) and the pending PV product of sub-tile j - 1; it reads the K fragments of sub-tile
+      // j + 1 (after the barrier that makes its stage resident), issues the PV MFMAs of sub-tile
+      // j - 1, then the score MFMAs of sub-tile j + 1 (into sn) with the probabilities and the
+      // V^T reads of sub-tile j between them.
+      // The probabilities are speculative: they are taken against the row's current reference
+      // (the max of the piece's first sub-tile, raised when needed) without waiting for the
+      // sub-tile's own row max. When this lane's sum of them passes 2^8 (some score rose about 8
+      // log2 units above the reference), the sub-tile takes a slow path that moves the reference
+      // to the row max, rescales O and l, and recomputes its probabilities from its scores, which
+      // stay in registers until the check. On ordinary inputs no row max is taken in the loop.
       // The last step's score MFMAs read a stale ring slot; those scores are never used. K is
       // read one sub-tile ahead of V, so at a barrier two stages are in use. The loop runs NPH
       // steps per iteration (one turn of the ring), so ring slots and sub-tile offsets are
       // compile-time constants and every LDS address is a register plus an immediate.
       constexpr int NPH = NBUF * SPS;
+      float mc = 0.f;  // the reference, in log2 units (a score times c)
+      // probabilities of score registers 4Q..4Q+3 against mc, rounded to bf16 into the P^T
+      // operand and added (as rounded) to ps[Q % 2]: four exponent arguments, four exponentials,
+      // then the packing, so that no result is used right after the instruction that makes it
+      auto pexp4 = [&](const f32x16& sc, float (&ps)[2], int q) {
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        const bf16x2 one = {(bf16)1.f, (bf16)1.f};
+        float x[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = fmaf(sc[4 * q + i], A.c, -mc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = tt_exp2(x[i]);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          bf16x2 pr;
+          pr[0] = (bf16)x[2 * h];
+          pr[1] = (bf16)x[2 * h + 1];
+          if constexpr (EPL == 8) {
+            pf[q / 2][4 * (q % 2) + 2 * h] = pr[0];
+            pf[q / 2][4 * (q % 2) + 2 * h + 1] = pr[1];
+          }
+          ps[q % 2] = __builtin_amdgcn_fdot2_f32_bf16(pr, one, ps[q % 2], false);
+        }
+      };
+      auto mask_at = [&](f32x16& sc, int j) {
+        const int kvalid = nkeys - 32 * j;
+        const int kfirst = ka + 32 * j;  // index in the unit's key list of the sub-tile's first key
+        if (kvalid < 32 || (CAUSAL && kfirst + 32 > P)) mask(sc, kvalid, kfirst);
+      };
+      auto rowmax = [&](const f32x16& sc) {
+        float mx = sc[0];
+#pragma unroll
+        for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sc[e]);
+        return tt_max_halves(mx);
+      };
       if (active) {
+        // prologue: the scores of sub-tile 0 and, from their row max, the row's first reference
+        // (-inf: no key of the piece is visible to the row, its probabilities are all 0)
         frag kf[NQK];
         kread_c(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, kf);
         tt_static_for<NQK>([&](auto i) { qk_mma(kf, sa, i); });
+        mask_at(sa, 0);
+        const float mx = rowmax(sa);
+        mc = (mx == -INFINITY) ? 0.f : mx * A.c;
       }
       auto step = [&](auto ph, auto act, int j, f32x16& sc, f32x16& sn) {
         constexpr int PH = decltype(ph)::value, PN = PH + 1;
@@ -634,10 +683,29 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_partial(Args<T, D> A) {
         if constexpr (!decltype(act)::value) return;  // a wave without query rows: loads only
         frag kf[NQK];
         kread_c(std::integral_constant<int, BUFN>{}, std::integral_constant<int, KTN>{}, kf);
-        const float mc = row_max(sc, j, std::true_type{});
-        expo(sc, mc, std::true_type{}, kf, sn, [&](auto l) {
-          vread_c(std::integral_constant<int, BUF>{}, std::integral_constant<int, KT>{}, l);
-        });
+        if (j > 0) mask_at(sc, j);
+        tt_static_for<NPV>(pv_mma);
+        float ps[2] = {0.f, 0.f};
+        tt_interleave<NQK, 4, NPV>([&](auto i) { qk_mma(kf, sn, i); },
+                                   [&](auto q) { pexp4(sc, ps, decltype(q)::value); },
+                                   [&](auto l) {
+                                     vread_c(std::integral_constant<int, BUF>{}, std::integral_constant<int, KT>{}, l);
+                                   });
+        // speculation check (see above); the PV MFMAs of j - 1 have all been issued, so O can be
+        // rescaled here before the PV product of j adds to it
+        if (__builtin_expect(__ballot(ps[0] + ps[1] > RESCALE_SUM) != 0, 0)) {
+          const float mcn = fmaxf(mc, rowmax(sc) * A.c);
+          const float alpha = tt_exp2(mc - mcn);
+          lrun *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) o[dt][q] *= alpha;
+          mc = mcn;
+          ps[0] = ps[1] = 0.f;
+          tt_static_for<4>([&](auto q) { pexp4(sc, ps, decltype(q)::value); });
+        }
+        lrun += ps[0] + ps[1];
       };
       auto run = [&](auto act) {
         for (int j0 = 0; j0 < nsub; j0 += NPH) {
@@ -653,6 +721,7 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_partial(Args<T, D> A) {
       if (active) run(std::true_type{});
       else run(std::false_type{});
       if (active) tt_static_for<NPV>(pv_mma);  // the last sub-tile's PV product
+      mc_final = mc;
     } else {
       // One sub-tile after the other: scores, softmax, PV product.
       for (int j = 0; j < nsub; ++j) {
@@ -716,7 +785,8 @@ __global__ __launch_bounds__(AT_THREADS, 1) void attn_partial(Args<T, D> A) {
               for (int e = 0; e < 4; ++e) v[e] = (PT)(o[dt][4 * jg + e] * inv);
               *reinterpret_cast<pvec*>(wp + (dt * 4 + jg) * 256) = v;
             }
-          if (hh2 == 0) A.ws_ml[slot * R + row] = make_float2(mrun, ltot);
+          const float ref = PIPE ? mc_final : mrun * A.c;
+          if (hh2 == 0) A.ws_ml[slot * R + row] = make_float2(ltot == 0.f ? -INFINITY : ref, ltot);
         }
       }
     }
@@ -748,8 +818,8 @@ __device__ __forceinline__ void block_sum2(int64_t& a, int64_t& b) {
   }
 }
 
-// Split-K merge of a unit's normalised partials: O = sum_k e^(m_k - M) l_k Ohat_k /
-// sum_k e^(m_k - M) l_k. Workgroup = CB_RB query rows x QB quads (4 consecutive output elements)
+// Split-K merge of a unit's normalised partials (references r_k in log2 units, R their max):
+// O = sum_k 2^(r_k - R) l_k Ohat_k / sum_k 2^(r_k - R) l_k. Workgroup = CB_RB query rows x QB quads (4 consecutive output elements)
 // of one unit, rows fastest, so the 16-byte partial loads of consecutive threads are contiguous; thread (row rr, quad qq, group sg) owns one quad of its row and the
 // partials of workgroups wf + sg, wf + sg + NSG, ... (CB loads in flight together); the NSG
 // groups of a row are merged in the order sg = 0, 1, ... through LDS, a fixed order, so the
@@ -813,13 +883,13 @@ __global__ __launch_bounds__(CB_THREADS) void attn_combine(Args<T, D> A) {
     float bm = M;
 #pragma unroll
     for (int k = 0; k < CB; ++k) bm = fmaxf(bm, ml[k].x);
-    const float rs = (M == -INFINITY) ? 0.f : tt_exp2((M - bm) * A.c);
+    const float rs = (M == -INFINITY) ? 0.f : tt_exp2(M - bm);
     L *= rs;
 #pragma unroll
     for (int e = 0; e < VPT; ++e) acc[e] *= rs;
 #pragma unroll
     for (int k = 0; k < CB; ++k) {
-      const float wk = (ml[k].x == -INFINITY) ? 0.f : tt_exp2((ml[k].x - bm) * A.c) * ml[k].y;
+      const float wk = (ml[k].x == -INFINITY) ? 0.f : tt_exp2(ml[k].x - bm) * ml[k].y;
       L += wk;
       const PT* pv = reinterpret_cast<const PT*>(&ov[k]);
 #pragma unroll
@@ -840,8 +910,8 @@ __global__ __launch_bounds__(CB_THREADS) void attn_combine(Args<T, D> A) {
       const float m2 = gm[rr][q][qq];
       if (m2 == -INFINITY) continue;
       const float bm = fmaxf(M, m2);
-      const float r1 = (M == -INFINITY) ? 0.f : tt_exp2((M - bm) * A.c);
-      const float r2 = tt_exp2((m2 - bm) * A.c);
+      const float r1 = (M == -INFINITY) ? 0.f : tt_exp2(M - bm);
+      const float r2 = tt_exp2(m2 - bm);
       L = L * r1 + gl[rr][q][qq] * r2;
 #pragma unroll
       for (int e = 0; e < VPT; ++e) acc[e] = acc[e] * r1 + ga[rr][q][qq][e] * r2;

@@ -117,6 +117,8 @@ __device__ __forceinline__ void tt_wait_vmem() {
 // s_waitcnt immediate for "vmcnt(0)" alone (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
 // in 6:4, lgkmcnt in 11:8; the other counters at their maxima)
 #define TT_WAIT_VMCNT0 0x0F70
+// ... and for "lgkmcnt(0)" alone (vmcnt 63, expcnt 7)
+#define TT_WAIT_LGKMCNT0 0xC07F
 
 #define TT_LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
