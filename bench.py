@@ -287,9 +287,9 @@ def main():
     ws_attn = torch.empty(bmd.workspace_bytes("tt_block_attn", B=wl.B, S=wl.S, Hq=wl.Hq, Hkv=wl.Hkv, D=wl.D,
                                               ctx_rows=wl.ctx_rows, max_prefix=wl.max_prefix),
                           dtype=torch.uint8, device=dev)
-    ws_um = torch.empty(max(256, bmd.workspace_bytes("tt_confidence_unmask", B=wl.B, S=wl.S, V=wl.V)),
+    ws_um = torch.zeros(max(256, bmd.workspace_bytes("tt_confidence_unmask", B=wl.B, S=wl.S, V=wl.V)),
                         dtype=torch.uint8, device=dev)
-    ws_fu = torch.empty(max(256, bmd.workspace_bytes("tt_lmhead_unmask", B=wl.B, S=wl.S, H=wl.H, V=wl.V)),
+    ws_fu = torch.zeros(max(256, bmd.workspace_bytes("tt_lmhead_unmask", B=wl.B, S=wl.S, H=wl.H, V=wl.V)),
                         dtype=torch.uint8, device=dev)
 
     if args.copy_calib:

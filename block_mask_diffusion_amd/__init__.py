@@ -88,12 +88,15 @@ def _sampler(kind: str, gamma: float, temperature: float) -> "_lib.Sampler":
     return _lib.Sampler(_lib.SAMPLER_KINDS[kind], float(gamma), float(temperature))
 
 
-def _workspace(nbytes: int, workspace: Optional[torch.Tensor], device) -> torch.Tensor:
+def _workspace(nbytes: int, workspace: Optional[torch.Tensor], device, zeroed: bool = False) -> torch.Tensor:
+    """A caller's workspace, checked for size, or a new one (zero-filled when `zeroed`: the
+    unmasking calls keep arrival counters, zero between calls, at its start)."""
     if workspace is not None:
         _need(workspace.is_cuda and workspace.numel() * workspace.element_size() >= nbytes,
               "workspace too small")
         return workspace
-    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    alloc = torch.zeros if zeroed else torch.empty
+    return alloc(max(nbytes, 256), dtype=torch.uint8, device=device)
 
 
 def tt_block_attn(q: torch.Tensor, k_blk: torch.Tensor, v_blk: torch.Tensor,
@@ -198,7 +201,7 @@ def tt_confidence_unmask(logits: torch.Tensor, tokens: torch.Tensor, mask_bits: 
     args = [_ptr(logits), _ptr(tokens), _ptr(mask_bits), _ptr(n_masked), _ptr(conf_out), _ptr(pred_out),
             B, S, V, int(step), int(num_steps), float(gamma), int(mask_id)]
     _check(lib.tt_confidence_unmask(*args, None, ctypes.byref(n), None), "tt_confidence_unmask")
-    ws = _workspace(n.value, workspace, logits.device)
+    ws = _workspace(n.value, workspace, logits.device, zeroed=True)
     n2 = ctypes.c_size_t(ws.numel() * ws.element_size())
     _check(lib.tt_confidence_unmask(*args, _ptr(ws), ctypes.byref(n2), _stream(stream)), "tt_confidence_unmask")
 
@@ -239,7 +242,7 @@ def tt_unmask_sample(logits: torch.Tensor, tokens: torch.Tensor, mask_bits: torc
     args = [_ptr(logits), _ptr(tokens), _ptr(mask_bits), _ptr(n_masked), _ptr(conf_out), _ptr(pred_out),
             B, S, V, int(step), int(num_steps), ctypes.byref(sm), int(mask_id)]
     _check(lib.tt_unmask_sample(*args, None, ctypes.byref(n), None), "tt_unmask_sample")
-    ws = _workspace(n.value, workspace, logits.device)
+    ws = _workspace(n.value, workspace, logits.device, zeroed=True)
     n2 = ctypes.c_size_t(ws.numel() * ws.element_size())
     _check(lib.tt_unmask_sample(*args, _ptr(ws), ctypes.byref(n2), _stream(stream)), "tt_unmask_sample")
 
@@ -283,6 +286,6 @@ def tt_lmhead_unmask(hidden: torch.Tensor, w: torch.Tensor, tokens: torch.Tensor
             _ptr(conf_out), _ptr(pred_out), B, S, H, V, int(step), int(num_steps), ctypes.byref(sm), int(mask_id),
             _dtype(hidden)]
     _check(lib.tt_lmhead_unmask(*args, None, ctypes.byref(n), None), "tt_lmhead_unmask")
-    ws = _workspace(n.value, workspace, hidden.device)
+    ws = _workspace(n.value, workspace, hidden.device, zeroed=True)
     n2 = ctypes.c_size_t(ws.numel() * ws.element_size())
     _check(lib.tt_lmhead_unmask(*args, _ptr(ws), ctypes.byref(n2), _stream(stream)), "tt_lmhead_unmask")

@@ -12,4 +12,4 @@ extern "C" const char* tt_status_string(int status) {
   }
 }
 
-extern "C" int tt_abi_version(void) { return (1 << 16) | 1; }
+extern "C" int tt_abi_version(void) { return (1 << 16) | 2; }

@@ -22,7 +22,14 @@
  *   - Workspace protocol (calls that take one): with workspace == NULL the call stores the
  *     required byte count in *workspace_bytes, returns TT_OK and launches nothing. Otherwise
  *     *workspace_bytes must hold the size of `workspace` (>= the required size, else
- *     TT_ERR_WORKSPACE); the workspace needs no initialisation and is scratch afterwards.
+ *     TT_ERR_WORKSPACE). The attention calls' workspace needs no initialisation and is scratch
+ *     afterwards. The unmasking calls' workspace (tt_confidence_unmask, tt_unmask_sample,
+ *     tt_lmhead_unmask) starts with arrival counters, 64 bytes apart, for the B blocks and the
+ *     B*S rows: its first align256(64 * (B + B*S)) bytes must be zero at entry, every call leaves
+ *     them zero, and the rest is scratch. So zero-fill such a workspace before its first use, and
+ *     again before a call with a larger B * (S + 1) than the calls before it on that workspace
+ *     (its counters then cover bytes that held records). It must be 256-byte aligned (else
+ *     TT_ERR_ARG).
  */
 #ifndef TT_H
 #define TT_H
@@ -159,7 +166,10 @@ int tt_lmhead_logits(const void* hidden, const void* w, float* logits,
  *   [0, V), num_steps <= 0, step outside [0, num_steps), NaN gamma; TT_ERR_UNSUPPORTED for
  *   S > 64; TT_ERR_WORKSPACE; TT_ERR_HIP. Any finite or infinite gamma is legal (gamma > 1
  *   commits exactly the floor's k per step; gamma <= 0 commits every masked position).
- * Workspace: per-row, per-vocabulary-chunk partial reductions, sized from B*S and V.
+ * Workspace: the arrival counters (zero at entry, zero again at exit; see the workspace
+ *   protocol), then partial reductions of each row's vocabulary ranges and one per row, sized from
+ *   B, S and V. The step is one kernel: the last workgroup of a row to finish merges the row, and
+ *   the last row of a block to finish commits the block.
  */
 int tt_confidence_unmask(const float* logits, int32_t* tokens, uint64_t* mask_bits,
                          int32_t* n_masked, float* conf_out, int32_t* pred_out,
@@ -171,11 +181,13 @@ int tt_confidence_unmask(const float* logits, int32_t* tokens, uint64_t* mask_bi
  * memory: code under HIP graph capture, tight serving loops, harnesses that forbid allocation.
  *
  * Same arguments, results and errors as tt_confidence_unmask without the workspace: the call
- * keeps its per-row, per-vocabulary-chunk records in a scratch array of 2 MiB that the library
+ * keeps its arrival counters and partial reductions in a scratch array of 2 MiB that the library
  * holds on each device it runs on (until the process ends), and calls no allocator.
- * Limit: B * S * ceil(V / 4096) * 16 bytes <= 2 MiB (B * S <= 4096 at V = 131072); beyond it the
- * call returns TT_ERR_WORKSPACE and launches nothing. TT_ERR_HIP also when the scratch's device
- * address cannot be looked up. Nothing in the scratch needs to start at zero.
+ * Limit: B + B * S <= 8192 (B * S <= 7696 at S = 16; the records then fit at any V); beyond it
+ * the call returns TT_ERR_WORKSPACE and launches nothing. TT_ERR_HIP also when the scratch's
+ * device address cannot be looked up. The counters have a fixed place in the scratch: they are
+ * zero when the library is loaded and every call leaves them zero, whatever the sizes of the
+ * calls before it.
  * Every call on one GPU shares that GPU's scratch, which keeps the last call's contents: calls
  * that overlap in time on one GPU (other streams, other host threads) race, and the caller must
  * serialise them.
@@ -204,8 +216,8 @@ int tt_confidence_unmask_noalloc(const float* logits, int32_t* tokens, uint64_t*
  * Errors: those of tt_unmask_sample; TT_ERR_ARG also for null hidden / w, H <= 0, exactly one
  *   bias pointer NULL, hidden or w not 16-byte aligned; TT_ERR_UNSUPPORTED for dtype TT_F32,
  *   H % 64 != 0 or S > 64.
- * Workspace: one 16-byte record per (row, block of 32 to 128 vocabulary columns, by B*S) plus one
- *   per row, sized from B*S and V.
+ * Workspace: the arrival counters (as for tt_confidence_unmask), then one 16-byte record per
+ *   (row, block of 32 to 128 vocabulary columns, by B*S) plus one per row, sized from B*S and V.
  */
 int tt_lmhead_unmask(const void* hidden, const void* w, const int32_t* bias_tok,
                      const float* bias_val, int32_t* tokens, uint64_t* mask_bits,

@@ -106,11 +106,26 @@ def _um(ws=None, nbytes=0, **kw):
     return st, n.value
 
 
+def _counters(B, S=16):
+    """Arrival counters of the B blocks and B*S rows, 64 bytes apart, rounded up to 256 bytes."""
+    return -(-64 * (B + B * S) // 256) * 256
+
+
 def test_unmask_workspace_query():
+    # counters, then one 16-byte record per (row, range of 4096-entry chunks) when a row is split
+    # (into up to ceil(V / 4096) ranges, so that rows x ranges reaches 1024), then one per row
     st, n = _um()
-    assert st == 0 and n == 16 * 32 * 16        # rows x 4096-entry chunks x 16 bytes
+    assert st == 0 and n == _counters(1) + 16 * 32 * 16 + 16 * 16        # 16 rows x 32 ranges
     st, n = _um(B=32, V=1000)
-    assert st == 0 and n == 512 * 1 * 16
+    assert st == 0 and n == _counters(32) + 512 * 16                     # one chunk: no split
+    st, n = _um(B=65, S=1, V=4097)
+    assert st == 0 and n == _counters(65, 1) + 65 * 2 * 16 + 65 * 16     # 65 rows x 2 ranges
+    st, n = _um(B=8, V=131072)
+    assert st == 0 and n == _counters(8) + 128 * 8 * 16 + 128 * 16       # 8 ranges of 4 chunks
+    st, n = _um(B=32, V=131072)
+    assert st == 0 and n == _counters(32) + 512 * 2 * 16 + 512 * 16      # 2 ranges of 16 chunks
+    st, n = _um(B=200, V=131072)
+    assert st == 0 and n == _counters(200) + 3200 * 16                   # 3200 rows >= 1024: no split
     assert _um(ws=P, nbytes=10)[0] == _lib.TT_ERR_WORKSPACE
 
 
@@ -142,24 +157,25 @@ def _fu(ws=None, nbytes=0, **kw):
 
 
 def test_fused_workspace_query():
-    # records per row: 64 columns each for up to 16 rows, 128 beyond; plus one per row
-    for B, cols in ((1, 64), (4, 128), (5, 128), (32, 128)):
+    # the B arrival counters (rounded up to 256 bytes); records per row: 64 columns each for up to
+    # 16 rows, 128 beyond; plus one per row
+    for B, cols in ((1, 64), (4, 128), (5, 128), (32, 128), (65, 128)):
         M = 16 * B
         st, n = _fu(B=B)
-        assert st == 0 and n == M * (131072 // cols) * 16 + M * 16, (B, n)
+        assert st == 0 and n == _counters(B) + M * (131072 // cols) * 16 + M * 16, (B, n)
     # small vocabularies: the LDS-staged kernel's tile is 64 VT rows with 16 VT columns per
     # record, VT the widest of 4, 2, 1 whose grid (vocabulary tiles x 16-row blocks) reaches 512;
     # up to 128 rows it runs when V <= 32768 and V * rows <= 2^21
     st, n = _fu(V=1000)
-    assert st == 0 and n == 16 * 63 * 16 + 16 * 16      # VT = 1: ceil(1000 / 16) = 63 records per row
+    assert st == 0 and n == _counters(1) + 16 * 63 * 16 + 16 * 16      # VT = 1: ceil(1000 / 16) = 63 records per row
     st, n = _fu(B=4, V=16384)
-    assert st == 0 and n == 64 * 512 * 16 + 64 * 16     # VT = 2 (128 x 4 = 512 workgroups): 32 columns
+    assert st == 0 and n == _counters(4) + 64 * 512 * 16 + 64 * 16     # VT = 2 (128 x 4 = 512 workgroups): 32 columns
     st, n = _fu(B=8, V=16384)
-    assert st == 0 and n == 128 * 256 * 16 + 128 * 16   # VT = 4 (64 x 8 = 512 workgroups): 64 columns
+    assert st == 0 and n == _counters(8) + 128 * 256 * 16 + 128 * 16   # VT = 4 (64 x 8 = 512 workgroups): 64 columns
     st, n = _fu(B=8, V=16385)
-    assert st == 0 and n == 128 * 129 * 16 + 128 * 16   # V * rows above 2^21: the GEMM kernel, 128 columns
+    assert st == 0 and n == _counters(8) + 128 * 129 * 16 + 128 * 16   # V * rows above 2^21: the GEMM kernel, 128 columns
     st, n = _fu(B=9, V=16384)
-    assert st == 0 and n == 144 * 128 * 16 + 144 * 16   # 144 rows: the GEMM kernel
+    assert st == 0 and n == _counters(9) + 144 * 128 * 16 + 144 * 16   # 144 rows: the GEMM kernel
     assert _fu(ws=P, nbytes=10)[0] == _lib.TT_ERR_WORKSPACE
 
 

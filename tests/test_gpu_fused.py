@@ -289,10 +289,12 @@ def test_mask_bits_above_S_are_ignored(B, S):
     stray = np.array([int(g.integers(0, 1 << 62)) & ~valid for _ in range(B)], dtype=np.uint64)
     hid_d, w_d, bt_d, bv_d = dev(inp["hidden"]), dev(inp["w"]), dev(bt), dev(bv)
     need = bmd.workspace_bytes("tt_lmhead_unmask", B=B, S=S, H=128, V=wl.V)
+    counters = -(-64 * (B + B * S) // 256) * 256
     guard = 1 << 16
     res = []
     for bits in (st["mask_bits"], st["mask_bits"] | stray):
         ws = torch.full((need + guard,), 0xAB, dtype=torch.uint8, device="cuda")
+        ws[:counters] = 0   # the arrival counters start at zero; the rest of the workspace is scratch
         tok_d, bits_d = dev(st["tokens"]), dev(bits)
         nm = torch.empty(B, dtype=torch.int32, device="cuda")
         conf = torch.empty(wl.M, dtype=torch.float32, device="cuda")
@@ -306,6 +308,7 @@ def test_mask_bits_above_S_are_ignored(B, S):
         bmd.tt_confidence_unmask(logits, tok3, bits3, nm3, 0, wl.T, wl.gamma, wl.mask_id)
         torch.cuda.synchronize()
         assert torch.all(ws[need:] == 0xAB), "a record landed past the workspace"
+        assert torch.all(ws[:counters] == 0), "the arrival counters were not left at zero"
         res.append(dict(tok=tok_d.cpu().numpy(), bits=host_bits(bits_d), nm=nm.cpu().numpy(),
                         conf=conf.cpu().numpy(), pred=pred.cpu().numpy(), tok3=tok3.cpu().numpy(),
                         bits3=host_bits(bits3), nm3=nm3.cpu().numpy()))

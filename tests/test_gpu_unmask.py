@@ -114,3 +114,29 @@ def test_deterministic():
     for k in ("tokens", "mask_bits", "n_masked", "pred"):
         assert np.array_equal(outs[0][k], outs[1][k])
     assert np.array_equal(outs[0]["conf"].view(np.uint32), outs[1]["conf"].view(np.uint32))
+
+
+@pytest.mark.parametrize("B,S,V", [(3, 16, 131072), (70, 13, 9000)])
+def test_one_workspace_across_a_block(B, S, V):
+    """One caller workspace serves every step of a block: the arrival counters at its start are
+    zero before the first call and are left zero by each call, so every step equals the same step
+    on a fresh zero-filled workspace. B = 3 splits each row into 16 ranges of 2 chunks (row and
+    block tickets); B = 70 splits its 910 rows of 3 chunks (the last one ragged) into 2 ranges."""
+    wl = synth.workload(1, B=B, S=S, V=V, partial_init=True)
+    wl.wid = 1700 + B
+    logits = dev(synth.direct_logits(wl))
+    st = synth.initial_state(wl)
+    need = bmd.workspace_bytes("tt_confidence_unmask", B=B, S=S, V=V)
+    counters = -(-64 * (B + B * S) // 256) * 256
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    tok_a, bits_a = dev(st["tokens"]), dev(st["mask_bits"])
+    tok_b, bits_b = dev(st["tokens"]), dev(st["mask_bits"])
+    for step in range(wl.T):
+        nm_a = torch.empty(B, dtype=torch.int32, device="cuda")
+        nm_b = torch.empty(B, dtype=torch.int32, device="cuda")
+        bmd.tt_confidence_unmask(logits, tok_a, bits_a, nm_a, step, wl.T, wl.gamma, wl.mask_id, workspace=ws)
+        bmd.tt_confidence_unmask(logits, tok_b, bits_b, nm_b, step, wl.T, wl.gamma, wl.mask_id)
+        torch.cuda.synchronize()
+        assert torch.all(ws[:counters] == 0), step
+        assert torch.equal(tok_a, tok_b) and torch.equal(bits_a, bits_b) and torch.equal(nm_a, nm_b), step
+    assert np.all(host_bits(bits_a) == 0)

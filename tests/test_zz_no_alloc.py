@@ -43,10 +43,20 @@ def test_noalloc_equals_the_workspace_call_twice_in_a_row():
 
 
 def test_noalloc_rejects_sizes_past_its_scratch():
-    wl = synth.workload(1, B=260)   # 4160 rows x 32 chunks x 16 B > 2 MiB
+    wl = synth.workload(1, B=482, V=4096)   # 482 + 482 * 16 = 8194 counters > 8192
     st = synth.initial_state(wl)
     lg = torch.zeros((wl.M, wl.V), dtype=torch.float32, device="cuda")
     nm = torch.empty(wl.B, dtype=torch.int32, device="cuda")
     with pytest.raises(bmd.TTError) as e:
         bmd.tt_confidence_unmask_noalloc(lg, dev(st["tokens"]), dev(st["mask_bits"]), nm, 0, 16, 0.8, 3)
     assert e.value.status == -3
+
+
+def test_noalloc_at_its_largest_size_then_small_again():
+    # 481 blocks of 16 (481 + 7696 = 8177 counters, the most that fit), then 2 blocks of 16 whose
+    # rows are split into 32 ranges: the counters of the second call lie where the first call's did
+    for wl in (synth.workload(2, B=481, V=4096), synth.workload(2, B=2, partial_init=True)):
+        wl.wid = 1600 + wl.B
+        ref, got = _both(wl, synth.direct_logits(wl), 0)
+        for k in ref:
+            assert np.array_equal(ref[k], got[k]), (wl.B, k)
