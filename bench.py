@@ -1,6 +1,6 @@
 """Benchmark of the TwoTower denoiser block step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1..4] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1..4] [--no-cpu-baseline] [--calls-only]
 
 One step = one pass of the whole hot path over one batch of blocks: block attention for every
 layer, the LM-head product, the synthetic logit spikes (input construction, not the method),
@@ -45,6 +45,10 @@ def parse():
     ap.add_argument("--workload", type=int, default=4, choices=[1, 2, 3, 4],
                     help="1-4: the batch-1 2K, batch-8 8K, ragged batch-32 and batch-4 128K six-layer workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calls-only", action="store_true",
+                    help="skip the step loops and the CPU baseline: per-call medians only (every unmasking "
+                         "call at step 0), for kernel traces of single calls; prints a per-call JSON line, "
+                         "not the benchmark line")
     ap.add_argument("--cpu-steps", type=int, default=2, help="oracle block-steps in the CPU sample")
     ap.add_argument("--copy-calib", action="store_true",
                     help="run a 1 GiB device copy first (calibrates HBM byte counters)")
@@ -357,10 +361,11 @@ def main():
         torch.cuda.synchronize()
         return start.elapsed_time(end), time.perf_counter() - t_wall
 
-    total_ms, wall = timed_loop(step, nm_hist)
-    total_ms_fu, _ = timed_loop(step_fused, nm_hist_fu)
-    print(f"bench: timed loops done ({total_ms / K:.3f} ms/step three-call, {total_ms_fu / K:.3f} fused)",
-          file=sys.stderr, flush=True)
+    if not args.calls_only:
+        total_ms, wall = timed_loop(step, nm_hist)
+        total_ms_fu, _ = timed_loop(step_fused, nm_hist_fu)
+        print(f"bench: timed loops done ({total_ms / K:.3f} ms/step three-call, {total_ms_fu / K:.3f} fused)",
+              file=sys.stderr, flush=True)
 
     # per-call medians, each call launched alone between two events: attention cycles through the
     # layers (each layer's cache is cold again by its next turn at the six-layer workload); the
@@ -409,9 +414,6 @@ def main():
             commits += int(np.sum(start_masked - nm[t]))
         return block_steps, commits
 
-    block_steps, commits = tally(nm_hist.cpu().numpy())
-    block_steps_fu, commits_fu = tally(nm_hist_fu.cpu().numpy())
-    sec, sec_fu = total_ms / 1e3, total_ms_fu / 1e3
     alg = algorithmic(wl)
     lm_gbs = alg["lm_bytes"] / (t_lm * 1e-6) / 1e9
     lm_tfs = alg["lm_flops"] / (t_lm * 1e-6) / 1e12
@@ -448,6 +450,30 @@ def main():
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(um_gbs / HBM_PEAK_GBS, 4), "traffic": None,
                 "algorithmic_bytes": um_bytes, "avg_launch_us": round(t_um, 2)}
 
+    kernels = {
+        "attn": {"us_per_layer": round(t_attn, 2), "GB_s": round(attn_gbs, 1),
+                 "hbm_frac": round(attn_gbs / HBM_PEAK_GBS, 4), "TFLOP_s": round(attn_tfs, 1),
+                 "mfma_frac": round(attn_tfs / MFMA_BF16_PEAK_TFS, 4)},
+        "lmhead": {"kernel": lmhead_kernel_name(wl.M, wl.H, wl.V, wl.dtype), "us": round(t_lm, 2),
+                   "GB_s": round(lm_gbs, 1), "hbm_frac": round(lm_gbs / HBM_PEAK_GBS, 4),
+                   "TFLOP_s": round(lm_tfs, 2), "mfma_frac": round(lm_tfs / MFMA_BF16_PEAK_TFS, 4),
+                   "attainable_frac": round(lm_tfs / lm_attain_tfs, 4)},
+        "unmask": {"us_step0": round(t_um, 2), "masked_rows_step0": int(init_masked.sum()),
+                   "GB_s": round(um_gbs, 1), "hbm_frac": round(um_gbs / HBM_PEAK_GBS, 4)},
+        "spikes_us": round(t_spk, 2),
+        "lmhead_unmask_us_step0": round(t_fu, 2),
+        "context_extend_us": round(t_ext, 2),
+    }
+    per_call = f"median of {NC} launches after 5 warm-ups, each between two HIP events on the launch stream"
+    if args.calls_only:
+        print(json.dumps({"per_call_only": True, "config": {"workload": f"w{wl.wid}: {wl.name}"},
+                          "kernels": kernels, "timing": {"per_call": per_call}}), flush=True)
+        return
+
+    block_steps, commits = tally(nm_hist.cpu().numpy())
+    block_steps_fu, commits_fu = tally(nm_hist_fu.cpu().numpy())
+    sec, sec_fu = total_ms / 1e3, total_ms_fu / 1e3
+
     cpu = None
     if want_cpu:
         print("bench: CPU baseline (the oracle) ...", file=sys.stderr, flush=True)
@@ -474,18 +500,7 @@ def main():
         "committed_tokens_per_s": round(commits / sec, 2),
         "roofline": roof,
         "cpu_baseline": cpu,
-        "kernels": {
-            "attn": {"us_per_layer": round(t_attn, 2), "GB_s": round(attn_gbs, 1),
-                     "hbm_frac": round(attn_gbs / HBM_PEAK_GBS, 4), "TFLOP_s": round(attn_tfs, 1),
-                     "mfma_frac": round(attn_tfs / MFMA_BF16_PEAK_TFS, 4)},
-            "lmhead": {"kernel": lmhead_kernel_name(wl.M, wl.H, wl.V, wl.dtype), "us": round(t_lm, 2),
-                       "GB_s": round(lm_gbs, 1), "hbm_frac": round(lm_gbs / HBM_PEAK_GBS, 4),
-                       "TFLOP_s": round(lm_tfs, 2), "mfma_frac": round(lm_tfs / MFMA_BF16_PEAK_TFS, 4),
-                       "attainable_frac": round(lm_tfs / lm_attain_tfs, 4)},
-            "unmask": {"us_step0": round(t_um, 2), "masked_rows_step0": int(init_masked.sum()),
-                       "GB_s": round(um_gbs, 1), "hbm_frac": round(um_gbs / HBM_PEAK_GBS, 4)},
-            "spikes_us": round(t_spk, 2),
-        },
+        "kernels": {k: v for k, v in kernels.items() if k not in ("lmhead_unmask_us_step0", "context_extend_us")},
         "fused_path": {
             "what": "same step with tt_lmhead_unmask (LM head with the vocabulary reduction in its epilogue, "
                     "spikes as its logit bias, logits never stored) in place of LM head + spikes + unmask",
@@ -504,8 +519,7 @@ def main():
             "GB_s": round(ext_bytes / (t_ext * 1e-6) / 1e9, 1),
             "hbm_frac": round(ext_bytes / (t_ext * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
         },
-        "timing": {"per_call": f"median of {NC} launches after 5 warm-ups, each between two HIP events on "
-                               "the launch stream, after the step loops",
+        "timing": {"per_call": per_call + ", after the step loops",
                    "step_loop": f"{K} steps between two events, no per-call events inside"},
         "wall_s_timed": round(wall, 3),
         "input_gen_s": round(gen_s, 1),
