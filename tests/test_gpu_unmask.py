@@ -80,6 +80,18 @@ def test_odd_shapes(V, mask_id, S, B):
     _run_and_compare(wl, logits, 4)
 
 
+@pytest.mark.parametrize("B,S,V,partial", [(64, 16, 20000, False), (70, 16, 36867, True), (33, 31, 4097, True)])
+def test_one_workgroup_per_row(B, S, V, partial):
+    """From 1024 rows on, one workgroup streams a whole row: its whole chunks two at a time with
+    the next chunk's loads in flight (odd and even chunk counts), then the ragged last chunk, and
+    there is no row ticket. V = 36867 is odd (the scalar-load kernel); partly committed blocks
+    leave some rows unread; 1023 rows still split each row in two (one whole chunk, one ragged)."""
+    wl = synth.workload(0, B=B, S=S, V=V, mask_id=V // 3, partial_init=partial)
+    wl.wid = 400 + B
+    logits = synth.direct_logits(wl, noise_std=1.0)
+    _run_and_compare(wl, logits, 2)
+
+
 @pytest.mark.parametrize("gamma", [2.0, float("inf"), 0.0, -1.0])
 def test_gamma_extremes(gamma):
     wl = synth.workload(0)
