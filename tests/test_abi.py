@@ -139,6 +139,15 @@ def test_unmask_argument_errors(kw, code):
     assert _um(**kw)[0] == code
 
 
+def test_unmasking_workspaces_must_be_256_byte_aligned():
+    # the arrival counters at a workspace's start need 256-byte alignment; rejected before any launch
+    odd = ctypes.c_void_p(4096 + 16)
+    for call in (_um, _fu):
+        need = call()[1]
+        assert call(ws=odd, nbytes=need + 256)[0] == _lib.TT_ERR_ARG
+    assert _lib.load().tt_abi_version() == (1 << 16) | 2
+
+
 def test_unmask_any_gamma_is_legal():
     for g in (float("inf"), float("-inf"), 2.0, 0.0, -1.0):
         assert _um(gamma=g)[0] == 0
