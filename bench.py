@@ -199,14 +199,16 @@ def cpu_baseline(wl, host, steps):
 
 def lmhead_kernel_name(M, H, V, dtype="bf16"):
     """The kernel tt_lmhead_logits launches for these sizes: the library's own choice (lmhead.hip,
-    lm_use_lds / lm_bf16; gemm.hip, gemm_wm) written out, for the roofline's label."""
+    lm_use_lds / lm_bf16; gemm.hip, gemm_cfg) written out, for the roofline's label. The GEMM's
+    template arguments are <waves along M, MFMA tiles per wave along M, along the vocabulary>."""
     if dtype != "bf16":
         return "lmhead_kernel"
     if H % 64 == 0 and (M <= 16 or (M <= 128 and (V + 511) // 512 <= 64 and V * M <= 1 << 21)):
         return "lmhead_lds_kernel"
     if M > 16 and H % 64 == 0:
-        wm = 1 if (M <= 128 and (V + 511) // 512 > 64) else 2
-        return f"lmhead_gemm_kernel<{wm}>"
+        if (V + 511) // 512 <= 64 or M > 128:
+            return "lmhead_gemm_kernel<2, 4, 4>"      # 256 x 256 tile
+        return "lmhead_gemm_kernel<1, 2, 2>" if M <= 64 else "lmhead_gemm_kernel<1, 4, 4>"
     return "lmhead_kernel"
 
 

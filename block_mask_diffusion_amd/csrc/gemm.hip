@@ -21,25 +21,30 @@ constexpr int NXCD = 8;
 // row 8 (j / 4) + 4 (l / 32) + j % 4
 __device__ __forceinline__ int mrow(int lane, int j) { return 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3); }
 
-// Workgroup = 4 waves, each owning a 128 x 128 block of 4 x 4 MFMA 32x32x16 tiles (256
-// accumulators per lane, held in AGPRs; one wave per SIMD). Both operands go HBM/L2 -> LDS by
-// direct loads into a 2-deep ring of GM_KB = 64-wide k stages: each row contributes one whole
-// 128-byte line per stage, and the next stage's loads run while the current one is multiplied.
-// LDS -> registers in MFMA operand layout: a lane reads 16 bytes = 8 consecutive h of one row;
-// the 16-byte granules of row r are stored at slot g ^ ((r >> 1) & 7), so the 16 rows read by
-// 16 consecutive lanes hit 16 distinct 16-byte bank groups. The next k-step's fragments are read
-// while the current k-step's MFMAs run. The default tile is 256 hidden rows x 256 vocabulary
-// rows (2 x 2 waves); with two hidden-row blocks the workgroups of one vocabulary tile have
-// dispatch ids congruent modulo 8 (same XCD) and 8 apart, so W is fetched from HBM once (measured
-// with FETCH_SIZE). A 512 x 128 tile (W read by one workgroup only) measured slower: it doubles
-// the re-reads of the hidden rows from L2. Also measured and not faster at 512 rows: 32-wide
-// stages in a 4- or 5-deep ring (TT_GEMM_KB=32, TT_GM_NBUF=4 or 5 build the variant), the LDS
+// Workgroup = 4 waves, one per SIMD, each owning a block of TM x TN MFMA 32x32x16 tiles (16 TM TN
+// accumulators per lane, held in AGPRs). Both operands go HBM/L2 -> LDS by direct loads into a
+// ring of GM_KB = 64-wide k stages, as deep as the LDS holds (up to 4): each row contributes one
+// whole 128-byte line per stage, and the later stages' loads run while the current one is
+// multiplied. LDS -> registers in MFMA operand layout: a lane reads 16 bytes = 8 consecutive h of
+// one row; the 16-byte granules of row r are stored at slot g ^ ((r >> 1) & 7), so the 16 rows
+// read by 16 consecutive lanes hit 16 distinct 16-byte bank groups. The next k-step's fragments
+// are read while the current k-step's MFMAs run.
+// Tiles (hidden rows x vocabulary rows): 64 x 256 (1 x 4 waves of 2 x 2 tiles) up to 64 rows,
+// whose 40 KiB stages fit a 4-deep ring, so three stages of W stream ahead per CU (the product is
+// HBM-bound there; measured at 64 rows: 119 against 129-134 us for the fused call with the
+// 128 x 512 tile and its 2-deep ring); 128 x 512 (1 x 4 waves of 4 x 4) up to 128 rows; 256 x 256
+// (2 x 2 waves of 4 x 4) beyond. With two hidden-row blocks the workgroups of one vocabulary tile
+// have dispatch ids congruent modulo 8 (same XCD) and 8 apart, so W is fetched from HBM once
+// (measured with FETCH_SIZE); the 64 x 256 tile over two blocks (65 to 128 rows) measured slower
+// (175-193 against 129-142 us). A 512 x 128 tile (W read by one workgroup only) measured slower
+// at 512 rows: it doubles the re-reads of the hidden rows from L2. Also measured and not faster
+// at 512 rows: 32-wide stages in a 4- or 5-deep ring (TT_GEMM_KB=32 builds the variant), the LDS
 // reads pinned between the MFMAs of the previous k-step, and a per-workgroup rotation of the
 // k-stage order.
 #ifndef TT_GM_NBUF
-#define TT_GM_NBUF 2
+#define TT_GM_NBUF 4
 #endif
-constexpr int GM_KB = TT_GEMM_KB, GM_NBUF = TT_GM_NBUF;
+constexpr int GM_KB = TT_GEMM_KB, GM_NBUF = TT_GM_NBUF;  // the deepest ring the LDS holds, up to this
 constexpr int GM_ROWB = GM_KB * 2;                  // bytes per LDS row
 constexpr int GM_KS = GM_KB / 16;                   // MFMA k-steps per stage
 constexpr int GM_GPR = GM_KB / 8;                   // 16-byte granules per row
@@ -51,21 +56,23 @@ static_assert(GM_KS % 2 == 0, "k-steps are pipelined in pairs");
 // LDS bank sweep) land in 16 distinct 16-byte bank groups
 __device__ __forceinline__ int gm_swz(int r) { return (r / (256 / GM_ROWB)) % GM_GPR; }
 
-// WM waves along the hidden rows, 4 / WM along the vocabulary, each owning a 128 x 128 block:
-// tile BM = 128 WM hidden rows x BN = 128 (4 / WM) vocabulary rows.
+// WM waves along the hidden rows, 4 / WM along the vocabulary, each owning a block of TM x TN
+// MFMA tiles (32 TM hidden rows x 32 TN vocabulary rows): tile BM = 32 TM WM hidden rows x
+// BN = 32 TN (4 / WM) vocabulary rows.
 // RED = false: store the fp32 logits. RED = true: reduce each row's logits over the wave's 128
 // columns to one (max, lowest argmax, sum exp) record in red.parts[row][vtile * WN + wn]; the
 // logits never reach memory.
-template <int WM, bool RED>
+template <int WM, int TM, int TN, bool RED>
 __global__ __launch_bounds__(LM_THREADS, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void lmhead_gemm_kernel(
     const bf16* __restrict__ hidden, const bf16* __restrict__ w, float* __restrict__ logits, int M, int H,
     int V, int nvt, int nmb, TtRedArgs red) {
   constexpr int WN = LM_WAVES / WM;
-  constexpr int GM_BM = 128 * WM, GM_BN = 128 * WN;
+  constexpr int GM_BM = 32 * TM * WM, GM_BN = 32 * TN * WN;
+  constexpr int WROWS = 32 * TM, WCOLS = 32 * TN;  // one wave's block
   constexpr int ASTAGE = GM_BM * GM_ROWB, BSTAGE = GM_BN * GM_ROWB;  // bytes per stage
   constexpr int ACPW = ASTAGE / 1024 / LM_WAVES, BCPW = BSTAGE / 1024 / LM_WAVES;  // chunks per wave
   constexpr int PER_STAGE = ACPW + BCPW;  // load instructions per wave and stage
-  // ring depth: as deep as asked, within the LDS of one workgroup
+  // ring depth: as deep as the LDS of one workgroup holds, up to GM_NBUF
   constexpr int NBUF = GM_NBUF * (ASTAGE + BSTAGE) <= 160 * 1024 ? GM_NBUF : 160 * 1024 / (ASTAGE + BSTAGE);
   static_assert(NBUF >= 2 && (NBUF - 2) * PER_STAGE <= 63, "ring depth");
   typedef bf16x8 frag;
@@ -159,31 +166,36 @@ __global__ __launch_bounds__(LM_THREADS, 1) __attribute__((amdgpu_waves_per_eu(1
     tt_static_for<BCPW>([&](auto i) { tt_dma16_at<i * 1024, true>(bsrc[i] + k0, bb); });
   };
 
-  f32x16 acc[4][4];
+  f32x16 acc[TM][TN];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+  for (int mt = 0; mt < TM; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
+    for (int nt = 0; nt < TN; ++nt)
 #pragma unroll
       for (int j = 0; j < 16; ++j) acc[mt][nt][j] = 0.f;
 
   // fragments of k-step ks of the stage in buffer buf
-  auto read_frags = [&](int buf, int ks, frag (&fa)[4], frag (&fb)[4]) {
+  auto read_frags = [&](int buf, int ks, frag (&fa)[TM], frag (&fb)[TN]) {
     const unsigned char* a_s = sa[buf];
     const unsigned char* b_s = sb[buf];
+    const int gsl = 2 * ks + hh;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int ra = 128 * wm + 32 * t + l32, rb = 128 * wn + 32 * t + l32;
-      const int gsl = 2 * ks + hh;
-      fa[t] = *reinterpret_cast<const frag*>(a_s + ra * GM_ROWB + 16 * (gsl ^ gm_swz(ra)));
-      fb[t] = *reinterpret_cast<const frag*>(b_s + rb * GM_ROWB + 16 * (gsl ^ gm_swz(rb)));
+    for (int t = 0; t < (TM > TN ? TM : TN); ++t) {
+      if (t < TM) {
+        const int ra = WROWS * wm + 32 * t + l32;
+        fa[t] = *reinterpret_cast<const frag*>(a_s + ra * GM_ROWB + 16 * (gsl ^ gm_swz(ra)));
+      }
+      if (t < TN) {
+        const int rb = WCOLS * wn + 32 * t + l32;
+        fb[t] = *reinterpret_cast<const frag*>(b_s + rb * GM_ROWB + 16 * (gsl ^ gm_swz(rb)));
+      }
     }
   };
-  auto mma_step = [&](const frag (&fa)[4], const frag (&fb)[4]) {
+  auto mma_step = [&](const frag (&fa)[TM], const frag (&fb)[TN]) {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < TM; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
+      for (int nt = 0; nt < TN; ++nt)
         acc[mt][nt] = RED ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[nt], fa[mt], acc[mt][nt], 0, 0, 0)
                           : __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mt], fb[nt], acc[mt][nt], 0, 0, 0);
   };
@@ -203,7 +215,7 @@ __global__ __launch_bounds__(LM_THREADS, 1) __attribute__((amdgpu_waves_per_eu(1
     tt_lds_barrier();
     if (st + NBUF - 1 < nst) issue(st + NBUF - 1);
     const int buf = st % NBUF;
-    frag fa0[4], fb0[4], fa1[4], fb1[4];
+    frag fa0[TM], fb0[TN], fa1[TM], fb1[TN];
     read_frags(buf, 0, fa0, fb0);
 #pragma unroll
     for (int ks = 0; ks < GM_KS; ks += 2) {
@@ -218,23 +230,24 @@ __global__ __launch_bounds__(LM_THREADS, 1) __attribute__((amdgpu_waves_per_eu(1
     // The fused path multiplies W by the hidden rows (operands swapped), so each accumulator
     // tile holds logits transposed: lane l, register j of tile (mt, nt) is hidden row
     // 32 mt + l % 32 and vocabulary id cb + 32 nt + 8 (j / 4) + 4 (l / 32) + j % 4. A lane thus
-    // holds 64 of its row's 128 logits and lane l ^ 32 the other 64: the row reduction runs in
-    // registers, with one exchange between the two halves of the wave.
-    const int cb = v0 + 128 * wn;  // first vocabulary id of the block
+    // holds half of its row's WCOLS logits and lane l ^ 32 the other half: the row reduction runs
+    // in registers, with one exchange between the two halves of the wave.
+    constexpr int NVAL = 16 * TN, NG = NVAL / 8;  // logits per lane and row, in groups of 8
+    const int cb = v0 + WCOLS * wn;  // first vocabulary id of the block
     if (cb >= V) return;
     const int part = vtile * WN + wn;
     // only blocks that hold the mask id, the vocabulary's end or some row's bias entry (a wave-
     // uniform test) pay for the per-entry checks
-    const bool special = (red.mask_id >= cb && red.mask_id < cb + 128) || (cb + 128 > V);
-    int btok[4];
-    float bval[4];
+    const bool special = (red.mask_id >= cb && red.mask_id < cb + WCOLS) || (cb + WCOLS > V);
+    int btok[TM];
+    float bval[TM];
     bool hit = false;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const int mc = hrow(128 * wm + 32 * mt + l32);
+    for (int mt = 0; mt < TM; ++mt) {
+      const int mc = hrow(WROWS * wm + 32 * mt + l32);
       btok[mt] = red.bias_tok ? red.bias_tok[mc] : -1;
       bval[mt] = red.bias_tok ? red.bias_val[mc] : 0.f;
-      hit = hit || (btok[mt] >= cb && btok[mt] < cb + 128);
+      hit = hit || (btok[mt] >= cb && btok[mt] < cb + WCOLS);
     }
     // vocabulary id of v[k] below: increasing in k for a fixed lane
     auto vid = [&](int k) { return cb + 32 * (k >> 4) + 8 * ((k & 15) >> 2) + 4 * hh + (k & 3); };
@@ -244,10 +257,10 @@ __global__ __launch_bounds__(LM_THREADS, 1) __attribute__((amdgpu_waves_per_eu(1
     auto reduce_rows = [&](auto mode) {
       constexpr int MODE = decltype(mode)::value;
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        float v[64];
+      for (int mt = 0; mt < TM; ++mt) {
+        float v[NVAL];
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
+        for (int nt = 0; nt < TN; ++nt)
 #pragma unroll
           for (int j = 0; j < 16; ++j) v[16 * nt + j] = acc[mt][nt][j];
         if constexpr (MODE == 1) {
@@ -255,7 +268,7 @@ __global__ __launch_bounds__(LM_THREADS, 1) __attribute__((amdgpu_waves_per_eu(1
           // masks overflow the scalar registers)
           const int rel = btok[mt] - vid(0);
 #pragma unroll
-          for (int k = 0; k < 64; ++k) {
+          for (int k = 0; k < NVAL; ++k) {
             v[k] = (rel == vid(k) - vid(0)) ? v[k] + bval[mt] : v[k];
             if ((k & 7) == 7) __builtin_amdgcn_sched_barrier(0);
           }
@@ -263,49 +276,49 @@ __global__ __launch_bounds__(LM_THREADS, 1) __attribute__((amdgpu_waves_per_eu(1
           // as above, then the mask id and ids past the vocabulary's end become -inf
           const int rel = btok[mt] - vid(0), relm = red.mask_id - vid(0), relv = V - vid(0);
 #pragma unroll
-          for (int k = 0; k < 64; ++k) {
+          for (int k = 0; k < NVAL; ++k) {
             const int d = vid(k) - vid(0);
             const float x = (rel == d) ? v[k] + bval[mt] : v[k];
             v[k] = (relm == d || d >= relv) ? -INFINITY : x;
             if ((k & 3) == 3) __builtin_amdgcn_sched_barrier(0);
           }
         }
-        float mx[8];
+        float mx[NG];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
+        for (int q = 0; q < NG; ++q) {
           mx[q] = v[8 * q];
 #pragma unroll
           for (int e = 1; e < 8; ++e) mx[q] = fmaxf(mx[q], v[8 * q + e]);
         }
 #pragma unroll
-        for (int w2 = 4; w2 >= 1; w2 >>= 1)
+        for (int w2 = NG / 2; w2 >= 1; w2 >>= 1)
 #pragma unroll
           for (int q = 0; q < w2; ++q) mx[q] = fmaxf(mx[q], mx[q + w2]);
         const float rm = fmaxf(mx[0], tt_swap_halves(mx[0]));
         const bool empty = (rm == -INFINITY);
         const float mb = empty ? 0.f : rm * red.c;
-        int kf = 64;  // first k (lowest id) of this lane holding the maximum; 64 = none
+        int kf = NVAL;  // first k (lowest id) of this lane holding the maximum; NVAL = none
 #pragma unroll
-        for (int k = 63; k >= 0; --k) {
+        for (int k = NVAL - 1; k >= 0; --k) {
           kf = (v[k] == rm) ? k : kf;
           // keeps the compares next to their selects: hoisted, their masks overflow the SGPRs
           if ((k & 7) == 0) __builtin_amdgcn_sched_barrier(0);
         }
-        int key = (kf < 64) ? vid(kf) : INT32_MAX;
-        float sm[8];
+        int key = (kf < NVAL) ? vid(kf) : INT32_MAX;
+        float sm[NG];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
+        for (int q = 0; q < NG; ++q) {
           sm[q] = 0.f;
 #pragma unroll
           for (int e = 0; e < 8; ++e) sm[q] += tt_exp2(fmaf(v[8 * q + e], red.c, -mb));
         }
 #pragma unroll
-        for (int w2 = 4; w2 >= 1; w2 >>= 1)
+        for (int w2 = NG / 2; w2 >= 1; w2 >>= 1)
 #pragma unroll
           for (int q = 0; q < w2; ++q) sm[q] += sm[q + w2];
         const float rs = sm[0] + tt_swap_halves(sm[0]);  // same sum on both halves (commutative)
         key = min(key, tt_swap_halves_i(key));
-        const int rr = 128 * wm + 32 * mt + l32;
+        const int rr = WROWS * wm + 32 * mt + l32;
         if (hh == 0 && rr < nrows) {
           const int m = GATHER ? rowmap[rr] : m0 + rr;
           TtPartial p;
@@ -322,14 +335,14 @@ __global__ __launch_bounds__(LM_THREADS, 1) __attribute__((amdgpu_waves_per_eu(1
     else reduce_rows(std::integral_constant<int, 0>{});
   } else {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < TM; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const int v = v0 + 128 * wn + 32 * nt + l32;
+      for (int nt = 0; nt < TN; ++nt) {
+        const int v = v0 + WCOLS * wn + 32 * nt + l32;
         if (v >= V) continue;
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          const int m = m0 + 128 * wm + 32 * mt + mrow(lane, j);
+          const int m = m0 + WROWS * wm + 32 * mt + mrow(lane, j);
           if (m < M) logits[(size_t)m * V + v] = acc[mt][nt][j];
         }
       }
@@ -337,37 +350,50 @@ __global__ __launch_bounds__(LM_THREADS, 1) __attribute__((amdgpu_waves_per_eu(1
 }
 
 
-template <int WM, bool RED>
+template <int WM, int TM, int TN, bool RED>
 int gemm_launch(const void* hidden, const void* w, float* logits, int M, int H, int V, TtRedArgs red,
                 hipStream_t s) {
-  constexpr int BM = 128 * WM, BN = 128 * (LM_WAVES / WM);
+  constexpr int BM = 32 * TM * WM, BN = 32 * TN * (LM_WAVES / WM);
   const int nvt = (V + BN - 1) / BN;
   const int nmb = (M + BM - 1) / BM;
   const unsigned grid = (unsigned)(((nvt + NXCD - 1) / NXCD) * NXCD * nmb);
-  hipLaunchKernelGGL((lmhead_gemm_kernel<WM, RED>), dim3(grid), dim3(LM_THREADS), 0, s, (const bf16*)hidden,
+  hipLaunchKernelGGL((lmhead_gemm_kernel<WM, TM, TN, RED>), dim3(grid), dim3(LM_THREADS), 0, s, (const bf16*)hidden,
                      (const bf16*)w, logits, M, H, V, nvt, nmb, red);
   return tt_launch_status();
 }
 
 }  // namespace
 
-// Tile by M (measured at H = 2688, V = 131072): up to 128 hidden rows, 128 x 512 tiles (W read
-// once, few re-reads of the hidden rows); beyond, 256 x 256 (two hidden-row blocks share W in L2).
-// On a vocabulary of 32768 or less the 128 x 512 tiles give 64 workgroups or fewer, and the
-// 256 x 256 tile, with twice as many, is faster at any M (128 rows, V = 32768: 78.6 against
-// 94.7 us). Each output is the same chain of MFMAs in either tile.
-int gemm_wm(int M, int V) { return (M <= 128 && (V + 511) / 512 > 64) ? 1 : 2; }
+// Tile by M (measured at H = 2688, V = 131072): up to 64 hidden rows, 64 x 256 tiles, whose
+// 40 KiB stages leave room for a 4-deep ring (three stages of W in flight per CU); up to 128 rows,
+// 128 x 512 tiles (W read once, few re-reads of the hidden rows); beyond, 256 x 256 (two
+// hidden-row blocks share W in L2). On a vocabulary of 32768 or less the 128 x 512 tiles give 64
+// workgroups or fewer, and the 256 x 256 tile, with twice as many, is faster at any M (128 rows,
+// V = 32768: 78.6 against 94.7 us). Each output is the same chain of MFMAs in any tile.
+enum GemmCfg { GM_256x256, GM_128x512, GM_64x256 };
+GemmCfg gemm_cfg(int M, int V) {
+  if ((V + 511) / 512 <= 64 || M > 128) return GM_256x256;
+  return M <= 64 ? GM_64x256 : GM_128x512;
+}
+
+int tt_lm_gemm_cols(int M, int V) { return gemm_cfg(M, V) == GM_64x256 ? 64 : 128; }
 
 int tt_lm_gemm_launch(const void* hidden, const void* w, float* logits, int M, int H, int V, hipStream_t s) {
   const TtRedArgs none{nullptr, nullptr, -1, nullptr, 0};
-  if (gemm_wm(M, V) == 1) return gemm_launch<1, false>(hidden, w, logits, M, H, V, none, s);
-  return gemm_launch<2, false>(hidden, w, logits, M, H, V, none, s);
+  switch (gemm_cfg(M, V)) {
+    case GM_64x256: return gemm_launch<1, 2, 2, false>(hidden, w, logits, M, H, V, none, s);
+    case GM_128x512: return gemm_launch<1, 4, 4, false>(hidden, w, logits, M, H, V, none, s);
+    default: return gemm_launch<2, 4, 4, false>(hidden, w, logits, M, H, V, none, s);
+  }
 }
 
-// Fused variant: per-(row, 128-column block) reduction records instead of logits; red.nparts
-// must be ceil(V / 128).
+// Fused variant: per-(row, column block of one wave) reduction records instead of logits;
+// red.nparts must be ceil(V / tt_lm_gemm_cols(M, V)).
 int tt_lm_gemm_reduce_launch(const void* hidden, const void* w, int M, int H, int V, TtRedArgs red,
                              hipStream_t s) {
-  if (gemm_wm(M, V) == 1) return gemm_launch<1, true>(hidden, w, nullptr, M, H, V, red, s);
-  return gemm_launch<2, true>(hidden, w, nullptr, M, H, V, red, s);
+  switch (gemm_cfg(M, V)) {
+    case GM_64x256: return gemm_launch<1, 2, 2, true>(hidden, w, nullptr, M, H, V, red, s);
+    case GM_128x512: return gemm_launch<1, 4, 4, true>(hidden, w, nullptr, M, H, V, red, s);
+    default: return gemm_launch<2, 4, 4, true>(hidden, w, nullptr, M, H, V, red, s);
+  }
 }

@@ -539,9 +539,9 @@ int lm_bf16(const void* h, const void* w, float* o, int M, int H, int V, hipStre
 // Fused LM head + vocabulary reduction (bf16, H % 64 == 0): which kernel, and how many records per
 // row it writes. The same kernel as the logits path for each (M, V), so the accumulators are the
 // same: the LDS-staged kernel (16 VT columns per record) where lm_use_lds holds, else the GEMM
-// kernel (128 columns per record).
+// kernel (64 or 128 columns per record, by its tile).
 int tt_lm_reduce_nparts(int M, int H, int V) {
-  const int cols = lm_use_lds(M, H, V) ? 16 * lds_vt(M, V) : 128;
+  const int cols = lm_use_lds(M, H, V) ? 16 * lds_vt(M, V) : tt_lm_gemm_cols(M, V);
   return (V + cols - 1) / cols;
 }
 

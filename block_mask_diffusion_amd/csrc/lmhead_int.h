@@ -13,9 +13,12 @@ __attribute__((visibility("hidden"))) int tt_lm_gemm_launch(const void* hidden, 
                                                             float* logits, int M, int H, int V,
                                                             hipStream_t s);
 
+// Vocabulary columns of one wave's block in the GEMM kernel's tile for (M, V): 64 or 128.
+__attribute__((visibility("hidden"))) int tt_lm_gemm_cols(int M, int V);
+
 struct TtRedArgs;
 // Fused variant of the GEMM kernel: instead of logits, one (max, lowest argmax, sum exp) record
-// per (row, 128-column block) in red.parts (red.nparts = ceil(V / 128)).
+// per (row, column block of one wave) in red.parts (red.nparts = ceil(V / tt_lm_gemm_cols(M, V))).
 __attribute__((visibility("hidden"))) int tt_lm_gemm_reduce_launch(const void* hidden, const void* w,
                                                                    int M, int H, int V, TtRedArgs red,
                                                                    hipStream_t s);

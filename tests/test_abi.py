@@ -166,9 +166,9 @@ def _fu(ws=None, nbytes=0, **kw):
 
 
 def test_fused_workspace_query():
-    # the B arrival counters (rounded up to 256 bytes); records per row: 64 columns each for up to
-    # 16 rows, 128 beyond; plus one per row
-    for B, cols in ((1, 64), (4, 128), (5, 128), (32, 128), (65, 128)):
+    # the arrival counters; records per row: 64 columns each up to 64 rows (the LDS-staged kernel
+    # to 16 rows, then the GEMM's 64 x 256 tile), 128 beyond; plus one per row
+    for B, cols in ((1, 64), (2, 64), (4, 64), (5, 128), (32, 128), (65, 128)):
         M = 16 * B
         st, n = _fu(B=B)
         assert st == 0 and n == _counters(B) + M * (131072 // cols) * 16 + M * 16, (B, n)

@@ -62,14 +62,14 @@ def test_default_workload_is_the_largest_one_gpu_workload():
 
 
 def test_lmhead_kernel_label_follows_the_library_choice():
-    """The kernel tt_lmhead_logits picks (lmhead.hip lm_use_lds / gemm.hip gemm_wm), per workload."""
+    """The kernel tt_lmhead_logits picks (lmhead.hip lm_use_lds / gemm.hip gemm_cfg), per workload."""
     name = bench.lmhead_kernel_name
     assert name(16, 2688, 131072) == "lmhead_lds_kernel"          # batch 1
-    assert name(128, 2688, 131072) == "lmhead_gemm_kernel<1>"     # batch 8
-    assert name(512, 2688, 131072) == "lmhead_gemm_kernel<2>"     # ragged batch 32
-    assert name(64, 2688, 131072) == "lmhead_gemm_kernel<1>"      # batch 4
-    assert name(17, 2688, 131072) == "lmhead_gemm_kernel<1>"
+    assert name(128, 2688, 131072) == "lmhead_gemm_kernel<1, 4, 4>"     # batch 8
+    assert name(512, 2688, 131072) == "lmhead_gemm_kernel<2, 4, 4>"     # ragged batch 32
+    assert name(64, 2688, 131072) == "lmhead_gemm_kernel<1, 2, 2>"      # batch 4
+    assert name(17, 2688, 131072) == "lmhead_gemm_kernel<1, 2, 2>"
     assert name(64, 2688, 16384) == "lmhead_lds_kernel"           # small vocabulary
-    assert name(128, 256, 32768) == "lmhead_gemm_kernel<2>"
+    assert name(128, 256, 32768) == "lmhead_gemm_kernel<2, 4, 4>"
     assert name(16, 96, 2000) == "lmhead_kernel"
     assert name(16, 64, 1024, "f32") == "lmhead_kernel"
