@@ -41,7 +41,11 @@ def _bound(inp, dtype):
                                          # V M <= 2^21; else the GEMM, its 256 x 256 tile while V <= 32768
                                          (40, 256, 32768, "bf16"), (40, 256, 32769, "bf16"),
                                          (64, 2688, 16384, "bf16"), (128, 256, 16384, "bf16"),
-                                         (128, 256, 16385, "bf16"), (100, 256, 32769, "bf16")])
+                                         (128, 256, 16385, "bf16"), (100, 256, 32769, "bf16"),
+                                         # 17-64 rows above V = 32768: the GEMM's 64 x 256 tile with
+                                         # its 4-deep ring; ragged vocabulary tails
+                                         (33, 128, 65537, "bf16"), (64, 192, 40000, "bf16"),
+                                         (17, 64, 40961, "bf16")])
 def test_full_compare(M, H, V, dtype):
     wl = synth.workload(1, B=1, H=H, V=V, dtype=dtype)
     wl.B, wl.S = 1, M
