@@ -217,7 +217,7 @@ int tt_confidence_unmask_noalloc(const float* logits, int32_t* tokens, uint64_t*
  *   bias pointer NULL, hidden or w not 16-byte aligned; TT_ERR_UNSUPPORTED for dtype TT_F32,
  *   H % 64 != 0 or S > 64.
  * Workspace: the arrival counters (as for tt_confidence_unmask), then one 16-byte record per
- *   (row, block of 32 to 128 vocabulary columns, by B*S) plus one per row, sized from B*S and V.
+ *   (row, block of 16 to 128 vocabulary columns, by B*S and V) plus one per row, sized from B*S and V.
  */
 int tt_lmhead_unmask(const void* hidden, const void* w, const int32_t* bias_tok,
                      const float* bias_val, int32_t* tokens, uint64_t* mask_bits,
