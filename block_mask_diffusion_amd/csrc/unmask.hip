@@ -408,7 +408,7 @@ extern "C" int tt_unmask_sample(const float* logits, int32_t* tokens, uint64_t* 
   int st = unmask_check(tokens, mask_bits, n_masked, workspace_bytes, B, S, V, step, num_steps, mask_id,
                         sampler);
   if (st != TT_OK) return st;
-  if (S > 64) return TT_ERR_UNSUPPORTED;
+  if (S > 64 || V > INT32_MAX - UM_CHUNK) return TT_ERR_UNSUPPORTED;  // chunk indices stay in int
   if ((size_t)B * S * unmask_plan(B, S, V).nsplit > (size_t)INT32_MAX) return TT_ERR_UNSUPPORTED;
   st = tt_workspace_check(workspace, workspace_bytes, unmask_ws_bytes(B, S, V));
   if (st != 0) return st < 0 ? st : TT_OK;
@@ -427,7 +427,7 @@ extern "C" int tt_confidence_unmask_noalloc(const float* logits, int32_t* tokens
   size_t unused = 0;
   int st = unmask_check(tokens, mask_bits, n_masked, &unused, B, S, V, step, num_steps, mask_id, &sm);
   if (st != TT_OK) return st;
-  if (S > 64) return TT_ERR_UNSUPPORTED;
+  if (S > 64 || V > INT32_MAX - UM_CHUNK) return TT_ERR_UNSUPPORTED;
   const UmPlan p = unmask_plan(B, S, V);
   if (((size_t)B + (size_t)B * S) * UM_SLOT_BYTES > UM_SCRATCH_CNT ||
       p.split_bytes + p.row_bytes > UM_SCRATCH_BYTES - UM_SCRATCH_CNT)

@@ -161,10 +161,10 @@ int tt_lmhead_logits(const void* hidden, const void* w, float* logits,
  *   (in/out); mask_bits uint64 [B] (in/out; bit i = position i still masked); n_masked int32 [B]
  *   (out). conf_out fp32 [B*S] and pred_out int32 [B*S] are optional (NULL = not written); when
  *   given they receive (conf_i, pred_i) for positions in Mk and (-1.0f, -1) for the others.
- * Supported: 1 <= S <= 64.
+ * Supported: 1 <= S <= 64, V <= 2^31 - 4097.
  * Errors: TT_ERR_ARG for null required pointers, B <= 0, S <= 0, V < 2, mask_id outside
  *   [0, V), num_steps <= 0, step outside [0, num_steps), NaN gamma; TT_ERR_UNSUPPORTED for
- *   S > 64; TT_ERR_WORKSPACE; TT_ERR_HIP. Any finite or infinite gamma is legal (gamma > 1
+ *   S > 64 or a larger V; TT_ERR_WORKSPACE; TT_ERR_HIP. Any finite or infinite gamma is legal (gamma > 1
  *   commits exactly the floor's k per step; gamma <= 0 commits every masked position).
  * Workspace: the arrival counters (zero at entry, zero again at exit; see the workspace
  *   protocol), then partial reductions of each row's vocabulary ranges and one per row, sized from

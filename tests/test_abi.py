@@ -133,7 +133,7 @@ def test_unmask_workspace_query():
     (dict(lg=None), -1), (dict(tok=None), -1), (dict(bits=None), -1), (dict(nm=None), -1),
     (dict(B=0), -1), (dict(S=0), -1), (dict(V=1), -1), (dict(mask_id=-1), -1), (dict(mask_id=131072), -1),
     (dict(T=0), -1), (dict(step=16), -1), (dict(step=-1), -1), (dict(gamma=float("nan")), -1),
-    (dict(S=65), -2),
+    (dict(S=65), -2), (dict(V=2**31 - 4096, mask_id=3), -2),
 ])
 def test_unmask_argument_errors(kw, code):
     assert _um(**kw)[0] == code
