@@ -72,7 +72,10 @@ def test_full_vocab_workloads_stagewise(wid):
 
 
 @pytest.mark.parametrize("V,mask_id,S,B", [(2, 0, 16, 1), (2, 1, 1, 3), (1001, 1000, 64, 2), (4099, 0, 7, 5),
-                                           (8192, 4096, 33, 2), (131071, 3, 16, 2)])
+                                           (8192, 4096, 33, 2), (131071, 3, 16, 2),
+                                           # one row of one position in 32 ranges; 64-position
+                                           # blocks in 8 ranges of 2 chunks
+                                           (131072, 131071, 1, 1), (65536, 7, 64, 2)])
 def test_odd_shapes(V, mask_id, S, B):
     wl = synth.workload(0, V=V, mask_id=mask_id, S=S, B=B)
     wl.wid = 300 + V % 97
